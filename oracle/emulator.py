@@ -1,0 +1,172 @@
+"""Step-by-step CPU emulator of the FP8 attention method. TEST INFRASTRUCTURE ONLY (diagnostic).
+
+Not the parity reference (that is ``oracle.attention``). This follows the method's own steps in
+the order the pages give them, in numpy fp32 where the method works in fp32:
+
+1. per KV tile of ``tile_n`` keys: scores s (fp32) of the exact E4M3 dot products, masked -> -inf;
+2. tile row max in scaled log2 units mt = max(s) * c, c = fp32(scale * dq * dk * log2 e)
+   (q/k descales folded into the softmax scale: "Native FP8 (E4M3 Q/K/V) forward for Hopper",
+   Design, Descales);
+3. lazy rescale: the stored max m moves to mt only when m is -inf or mt - m > tau, and then the
+   running O and l are multiplied by alpha = 2^(m - mt) (the bound tau <= log2(448) - 8 keeps the
+   biased P below the E4M3 ceiling: sheared-forward fp8 page, "Correctness fix over #1:
+   rescale_threshold");
+4. p = 2^(s*c - m + bias), bias = 8 (the 2^8 pre-scale of P, Design "P in FP8" and the sheared
+   page's Summary), cast to E4M3 with round-to-nearest-even (saturating at 448, counted as a clip);
+5. l = alpha*l + sum(p)  (unrounded p by default);
+6. two-level PV: O_tile = P8 @ V for this tile alone, then O = alpha*O + O_tile (Design,
+   "Two-level PV accumulation");
+7. end of a KV range: O = O * dv / l, LSE = ln2 * (m + log2 l - bias) (bias removed from the LSE).
+
+Several splits over contiguous KV ranges are merged with ``oracle.combine``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import combine, e4m3_table, seqlens
+
+LOG2E = 1.4426950408889634
+E4M3_MAX = 448.0
+
+
+def e4m3_encode_rne(x: np.ndarray, saturate: bool = True) -> np.ndarray:
+    """float32 -> E4M3FN codes, round to nearest even (OCP definition: bias 7, 3 mantissa bits,
+    subnormal spacing 2^-9, max 448). Beyond 448: saturate to 448 (saturate=True) or NaN
+    (code 0x7F) when the value rounds past 448, i.e. |x| >= 464."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.abs(x)
+    code = np.zeros(a.shape, np.uint8)
+    nan = np.isnan(a)
+    # quantum of the binade containing a: 2^(e-3) for normals (e >= -6), 2^-9 for subnormals
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    q = np.exp2(e - 3.0)
+    n = a / q                                    # exact (power-of-two division)
+    r = np.floor(n)
+    frac = n - r
+    r = np.where((frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2) == 1)), r + 1, r)
+    v = r * q                                    # rounded magnitude, exact
+    # re-derive exponent/mantissa of the rounded value
+    big = v > E4M3_MAX
+    v = np.where(big, E4M3_MAX, v)
+    with np.errstate(divide="ignore"):
+        ev = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    sub = v < 2.0 ** -6
+    mant_sub = np.round(v / 2.0 ** -9).astype(np.int64)
+    mant_norm = np.round((v / np.exp2(ev) - 1.0) * 8.0).astype(np.int64)
+    efield = (ev + 7).astype(np.int64)
+    c = np.where(sub, mant_sub, (efield << 3) | mant_norm)
+    c = np.where(v == 0, 0, c)
+    code = c.astype(np.uint8)
+    if not saturate:
+        code = np.where(big, np.uint8(0x7F), code)
+    code = np.where(nan, np.uint8(0x7F), code)
+    return (code | sign).astype(np.uint8)
+
+
+def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_splits: int = 1,
+            l_from_rounded: bool = False, heads: Optional[list] = None, batches: Optional[list] = None,
+            stats: Optional[dict] = None):
+    """Run the method on every query row of the selected (batch, head) pairs.
+
+    Returns a dict {(b, h): (O [Sq_b, dv] float64, LSE [Sq_b] float64)}.
+    stats, if given, receives 'clipped' (number of P values that exceeded 448) and 'pmax'.
+    """
+    dec = e4m3_table()
+    B, Hq, Hkv, d, dv = inp.batch, inp.heads_q, inp.heads_kv, inp.d, inp.dv
+    g = Hq // Hkv
+    sq_all, sk_all = seqlens(inp)
+    scale = inp.softmax_scale if inp.softmax_scale and inp.softmax_scale > 0 else 1.0 / math.sqrt(d)
+
+    def desc(x, b, kvh):
+        if x is None:
+            return 1.0
+        a = np.asarray(x, np.float64)
+        return float(a) if a.ndim == 0 else float(a[b, kvh])
+
+    out = {}
+    clipped = 0
+    pmax = 0.0
+    for b in (batches if batches is not None else range(B)):
+        sq, sk = int(sq_all[b]), int(sk_all[b])
+        # gather this batch's Q rows and K/V rows (by token index)
+        if inp.cu_seqlens_q is not None:
+            q0 = int(inp.cu_seqlens_q[b])
+            qb = inp.q[q0:q0 + sq]
+        else:
+            qb = inp.q[b, :sq]
+        j = np.arange(sk)
+        if inp.block_table is not None:
+            pg = inp.block_table[b, j // inp.page_size]
+            kb = inp.k[pg, j % inp.page_size]
+            vb = inp.v[pg, j % inp.page_size]
+        elif inp.cu_seqlens_k is not None:
+            k0 = int(inp.cu_seqlens_k[b])
+            kb, vb = inp.k[k0:k0 + sk], inp.v[k0:k0 + sk]
+        else:
+            kb, vb = inp.k[b, :sk], inp.v[b, :sk]
+        i = np.arange(sq)
+        ip = i + sk - sq
+        hi = np.full(sq, sk)
+        wr = 0 if inp.causal else inp.window_right
+        if wr >= 0:
+            hi = np.minimum(hi, ip + wr + 1)
+        lo = np.zeros(sq, np.int64)
+        if inp.window_left >= 0:
+            lo = np.maximum(lo, ip - inp.window_left)
+        for h in (heads if heads is not None else range(Hq)):
+            kvh = h // g
+            c = np.float32(scale * desc(inp.q_descale, b, kvh) * desc(inp.k_descale, b, kvh) * LOG2E)
+            dvs = desc(inp.v_descale, b, kvh)
+            qf = dec[qb[:, h, :]]                        # [sq, d] exact
+            kf = dec[kb[:, kvh, :]]                      # [sk, d]
+            vf = dec[vb[:, kvh, :]]                      # [sk, dv]
+            ntiles = (sk + tile_n - 1) // tile_n
+            parts_o, parts_l = [], []
+            for s in range(num_splits):
+                t0, t1 = (s * ntiles) // num_splits, ((s + 1) * ntiles) // num_splits
+                m = np.full(sq, -np.inf, np.float32)
+                l = np.zeros(sq, np.float32)
+                o = np.zeros((sq, dv), np.float32)
+                for t in range(t0, t1):
+                    js = np.arange(t * tile_n, min((t + 1) * tile_n, sk))
+                    sc = (qf @ kf[js].T).astype(np.float32)          # exact dots, rounded to fp32
+                    vis = (js[None, :] >= lo[:, None]) & (js[None, :] < hi[:, None])
+                    sc = np.where(vis, sc, np.float32(-np.inf))
+                    mt = (sc.max(axis=1) * c).astype(np.float32)
+                    with np.errstate(invalid="ignore"):
+                        move = (mt - m) > np.float32(tau)
+                    alpha = np.where(move, np.exp2((m - np.where(move, mt, 0)).astype(np.float32)), np.float32(1.0))
+                    alpha = np.where(move & np.isneginf(m), np.float32(0.0), alpha).astype(np.float32)
+                    m = np.where(move, mt, m).astype(np.float32)
+                    mb = np.where(np.isneginf(m), np.float32(0.0), np.float32(bias) - m).astype(np.float32)
+                    x = (sc.astype(np.float64) * np.float64(c) + mb[:, None].astype(np.float64)).astype(np.float32)
+                    p = np.exp2(x).astype(np.float32)                 # masked: 2^-inf = 0
+                    p = np.where(vis & ~np.isneginf(m)[:, None], p, np.float32(0.0))
+                    if p.size:
+                        pmax = max(pmax, float(p.max()))
+                        clipped += int((p > E4M3_MAX).sum())
+                    p8 = dec[e4m3_encode_rne(p, saturate=True)]
+                    psum = p8.sum(axis=1) if l_from_rounded else p.astype(np.float64).sum(axis=1)
+                    l = (alpha * l + psum.astype(np.float32)).astype(np.float32)
+                    o_tile = (p8 @ vf[js]).astype(np.float32)
+                    o = (alpha[:, None] * o + o_tile).astype(np.float32)
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    on = np.where(l[:, None] > 0, o.astype(np.float64) * dvs / l[:, None], 0.0)
+                    ls = np.where(l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(np.where(l > 0, l, 1.0)) - bias), -np.inf)
+                parts_o.append(on)
+                parts_l.append(ls)
+            if num_splits == 1:
+                out[(b, h)] = (parts_o[0], parts_l[0])
+            else:
+                out[(b, h)] = combine(np.stack(parts_o), np.stack(parts_l))
+    if stats is not None:
+        stats["clipped"] = clipped
+        stats["pmax"] = pmax
+    return out
