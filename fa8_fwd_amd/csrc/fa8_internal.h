@@ -1,0 +1,53 @@
+// Internal interface between the host-side ABI (fa8_host.cpp) and the gfx950 kernels
+// (fa8_kernels.hip). Everything here is resolved on the host from fa8_fwd_params.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fa8 {
+
+struct KParams {
+  const uint8_t* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  int64_t q_bs, q_rs, q_hs;
+  int64_t k_bs, k_rs, k_hs;   // k_bs: page stride when paged
+  int64_t v_bs, v_rs, v_hs;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  const int32_t* table;
+  int64_t table_stride;
+  int32_t page_shift;         // log2(page_size); -1 when not paged
+  const float* dq; int64_t dq_sb, dq_sh;
+  const float* dk; int64_t dk_sb, dk_sh;
+  const float* dv; int64_t dv_sb, dv_sh;
+  float scale_log2;           // softmax_scale * log2(e)
+  int32_t batch, hq, hkv, g, max_sq, max_sk;
+  int32_t wl, wr;             // -1 = unbounded; wr = 0 when causal
+  int32_t causal;
+  void* out; int64_t o_bs, o_rs, o_hs; int32_t out_fp16;
+  float* lse; int64_t l_bs, l_hs, l_rs;
+  float* o_part; float* lse_part; int32_t nsplit;
+  int32_t nmb;                // row blocks per (batch, head) (decode) or per (batch, q head) (prefill)
+};
+
+struct CParams {
+  const float* o_part;
+  const float* lse_part;
+  int32_t nsplit, batch, max_sq, hq, dv;
+  const int32_t* cu_q;
+  void* out; int64_t o_bs, o_rs, o_hs; int32_t out_fp16;
+  float* lse; int64_t l_bs, l_hs, l_rs;
+};
+
+// Rows per workgroup of the prefill kernel and of the decode kernel.
+constexpr int kPrefillRows = 128;
+constexpr int kDecodeRows = 32;
+constexpr int kKvTile = 64;
+
+hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream);
+hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream);
+hipError_t launch_combine(const CParams& cp, hipStream_t stream);
+
+}  // namespace fa8

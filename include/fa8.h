@@ -1,0 +1,199 @@
+/*
+ * fa8.h: C ABI of an FP8 (E4M3) attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * Computes O = softmax(Q K^T * scale) V with E4M3FN Q/K/V, an online softmax in exp2 with lazy
+ * rescaling, P cast to E4M3 with a 2^8 bias, and two-level PV accumulation into fp32 O
+ * ("[Cute,Fwd,Sm90] Native FP8 (E4M3 Q/K/V) forward for Hopper", Summary and Design; the
+ * lazy-rescale bound log2(448) - 8 from "fp8 on the sheared forward", Correctness fix).
+ *
+ * General rules for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library never allocates,
+ *    frees, synchronizes, or copies device memory to the host (except the optional validator
+ *    enabled by the environment variable FA8_VALIDATE=1, which copies index arrays to the host
+ *    and therefore must not be used during stream capture).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
+ *    asynchronous. Every launch decision depends only on the host-side values in the arguments,
+ *    never on device data, so a call may be captured in a HIP graph and replayed.
+ *  - Q/K/V are E4M3FN bytes (OCP 8-bit float: bias 7, 3 mantissa bits, max 448, no infinities).
+ *    E5M2 or mixed formats cannot be expressed through this ABI.
+ *  - Strides are in ELEMENTS of the tensor (bytes for E4M3, 2-byte units for fp16/bf16 output,
+ *    4-byte units for fp32). The last dimension (d or dv) is always contiguous. Q/K/V base
+ *    pointers must be 16-byte aligned and their strides multiples of 16; output and LSE strides
+ *    must keep 8-byte alignment of every 4-element group (output strides multiples of 4).
+ *  - A status other than FA8_OK means nothing was launched; fa8_last_error() then returns a
+ *    thread-local message describing the problem.
+ *  - Contract violations that only device data can reveal are the caller's responsibility and
+ *    are undefined behaviour (out-of-bounds device reads or writes): a block table narrower than
+ *    ceil(seqused_k[b] / page_size) entries for some b, a page index >= the pool size, a
+ *    sequence length above max_seqlen_q / max_seqlen_k, or cu_seqlens that are not
+ *    nondecreasing. FA8_VALIDATE=1 checks what the ABI can see (lengths against the maxima,
+ *    monotone cu_seqlens, non-negative page indices; the pool size is not an argument) on host
+ *    copies and returns FA8_ERR_INVALID on a violation.
+ */
+#ifndef FA8_H
+#define FA8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA8_OK = 0,
+  FA8_ERR_INVALID = 1,      /* a bad argument: shape, stride, pointer, alignment, limit */
+  FA8_ERR_UNSUPPORTED = 2,  /* a valid request this library does not implement (e.g. (d, dv)) */
+  FA8_ERR_HIP = 3           /* the HIP runtime reported an error when launching */
+} fa8_status;
+
+typedef enum { FA8_OUT_BF16 = 0, FA8_OUT_FP16 = 1 } fa8_out_dtype;
+
+/* Keys per split granule of the split-KV decode (see fa8_fwd_decode_splitkv). */
+#define FA8_SPLIT_GRANULE 64
+/* Packed (query token, query head) rows per block of the split-KV decode. */
+#define FA8_DECODE_BLOCK_ROWS 32
+/* Largest number of splits fa8_fwd_decode_splitkv and fa8_combine accept. */
+#define FA8_MAX_SPLITS 256
+
+/*
+ * A dequantization scale ("descale") for Q, K or V: the real value of an element is its
+ * E4M3 value times the descale. The page's descales are 0-d or (batch, kv_heads), contiguous
+ * or broadcast, read in place ("Native FP8 ... for Hopper", Design, Descales):
+ *   ptr == NULL                  -> 1.0
+ *   stride_b == stride_h == 0    -> one scalar *ptr
+ *   otherwise                    -> ptr[b * stride_b + kv_head * stride_h] (fp32, device)
+ * Q's descale is indexed by the KV head of the query head (kv_head = h / (heads_q / heads_kv)).
+ * The q and k descales fold into the softmax scale, the v descale into the final normalization.
+ */
+typedef struct {
+  const float* ptr;
+  int64_t stride_b;
+  int64_t stride_h;
+} fa8_descale;
+
+/*
+ * Problem description shared by fa8_fwd_prefill, fa8_fwd_decode_splitkv and fa8_check_params.
+ *
+ * Q and O: fixed length [batch, max_seqlen_q, heads_q, d] (O: dv) addressed with
+ *   (q_batch_stride, q_row_stride, q_head_stride); or varlen [total_q, heads_q, d] when
+ *   cu_seqlens_q ([batch + 1] int32, device) is set: sequence b owns token rows
+ *   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and q_batch_stride is ignored.
+ * K and V: fixed length [batch, max_seqlen_k, heads_kv, d|dv]; varlen [total_k, heads_kv, d|dv]
+ *   with cu_seqlens_k; or paged [num_pages, page_size, heads_kv, d|dv] when block_table is set,
+ *   where *_batch_stride is the PAGE stride, and key j of sequence b lives in page
+ *   block_table[b * block_table_stride + j / page_size] at row j % page_size.
+ *   page_size must be a power of two.
+ * Key lengths: seqused_k[b] if set, else from cu_seqlens_k, else max_seqlen_k. Paged K/V
+ *   requires seqused_k.
+ * Masks (rows aligned bottom-right: query i of a sequence sits at key position
+ *   i' = i + Sk_b - Sq_b, so the newest query sees the whole sequence): key j is visible to
+ *   query i iff j < Sk_b, j <= i' + wr and j >= i' - wl, where wr = 0 if causal else
+ *   window_right (no bound if < 0) and wl = window_left (no bound if < 0). A row with no
+ *   visible key gets O = 0 and LSE = -inf.
+ * GQA: heads_q must be a multiple of heads_kv; query head h reads kv head h / (heads_q/heads_kv).
+ * softmax_scale: <= 0 selects 1/sqrt(d).
+ * lse (optional, fp32): natural-log log-sum-exp of the scaled scores per row, at
+ *   lse[b * lse_batch_stride + h * lse_head_stride + i * lse_row_stride] (fixed length) or
+ *   lse[h * lse_head_stride + (cu_seqlens_q[b] + i) * lse_row_stride] (varlen).
+ * (d, dv) must be one of (64,64), (96,96), (128,128), (192,192), (256,256), (192,128)
+ *   ("Native FP8 ... for Hopper", Supported); anything else is FA8_ERR_UNSUPPORTED.
+ * Sizes: every dimension >= 0 (an empty problem launches nothing and returns FA8_OK); batch < 2^16;
+ *   max_seqlen_q, max_seqlen_k < 2^30; heads < 2^16.
+ */
+typedef struct {
+  int32_t batch, heads_q, heads_kv, d, dv;
+  int32_t max_seqlen_q, max_seqlen_k;
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  int64_t v_batch_stride, v_row_stride, v_head_stride;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  const int32_t* seqused_k;
+  const int32_t* block_table;
+  int64_t block_table_stride;
+  int32_t page_size;
+  fa8_descale q_descale, k_descale, v_descale;
+  float softmax_scale;
+  int32_t causal, window_left, window_right;
+  void* out;                       /* fp16 or bf16 per out_dtype */
+  int64_t o_batch_stride, o_row_stride, o_head_stride;
+  int32_t out_dtype;               /* fa8_out_dtype */
+  float* lse;                      /* optional */
+  int64_t lse_batch_stride, lse_head_stride, lse_row_stride;
+} fa8_fwd_params;
+
+/*
+ * Full forward pass into p->out (and p->lse when set): one workgroup per block of query rows
+ * of one query head, looping over the visible KV tiles ("Native FP8 ... for Hopper", Design;
+ * the method's steps: FP8 Q K^T, scale and mask, lazy-rescaled exp2 softmax with the 2^8 P
+ * bias, E4M3 P, FP8 PV accumulated per KV tile and folded into fp32 O, v descale and 1/l at
+ * the end). Works for fixed, varlen and paged K/V.
+ */
+fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);
+
+/*
+ * Split-KV partial pass for decode-shaped problems ("Native FP8 ... for Hopper", Decode
+ * launches: a direct (head, split, batch) grid; the q heads sharing a KV head are packed into
+ * the rows of one tile). Writes, for every split s, the attention restricted to that split's
+ * keys, already normalized, plus its LSE:
+ *   o_partial  [num_splits, batch, max_seqlen_q, heads_q, dv] fp32, contiguous
+ *   lse_partial[num_splits, batch, max_seqlen_q, heads_q]     fp32, contiguous
+ * (fa8_decode_workspace_bytes gives the combined size). Rows past a sequence's own Sq_b are
+ * not written. Split partition: the query rows of one (batch, kv head) block see the keys of
+ * granules [g0, g1) of FA8_SPLIT_GRANULE keys (the union of their visible ranges, rounded out
+ * to granules); split s covers granules [g0 + floor(s*n/S), g0 + floor((s+1)*n/S)), n = g1-g0,
+ * intersected with each row's own visible keys. An empty split writes O = 0, LSE = -inf.
+ * Row blocks: the (query token i, query head h) pairs of one (batch, kv head) are packed as
+ * rows r = i * g + (h - kv_head * g), g = heads_q / heads_kv, and cut into blocks of
+ * FA8_DECODE_BLOCK_ROWS consecutive rows; each block is partitioned into splits on its own.
+ * p->out and p->lse are not touched; fa8_combine produces them.
+ * num_splits: 1 .. FA8_MAX_SPLITS.
+ */
+fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, float* o_partial,
+                                  float* lse_partial, void* stream);
+
+/*
+ * Merges split partials into the final output: LSE = log sum_s exp(LSE_s),
+ * O = sum_s exp(LSE_s - LSE) * O_s, written as fp16/bf16 (round to nearest even). Rows whose
+ * splits are all empty get O = 0 and LSE = -inf. The split-KV combine is part of each decode
+ * step ("Native FP8 ... for Hopper", Performance). Layouts of o_partial / lse_partial as for
+ * fa8_fwd_decode_splitkv; out/lse addressing as in fa8_fwd_params (cu_seqlens_q may be NULL
+ * for fixed-length rows; lse may be NULL).
+ */
+fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t num_splits,
+                       int32_t batch, int32_t max_seqlen_q, const int32_t* cu_seqlens_q,
+                       int32_t heads_q, int32_t dv, void* out, int64_t o_batch_stride,
+                       int64_t o_row_stride, int64_t o_head_stride, int32_t out_dtype, float* lse,
+                       int64_t lse_batch_stride, int64_t lse_head_stride, int64_t lse_row_stride,
+                       void* stream);
+
+/* Runs the host-side validation of fa8_fwd_prefill (num_splits == 0) or of
+ * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything. Needs no GPU. */
+fa8_status fa8_check_params(const fa8_fwd_params* p, int32_t num_splits);
+
+/* Split count for fa8_fwd_decode_splitkv from host-known values only ("Launch choices depend
+ * only on host-known values", Decode launches): enough (batch * heads_kv * splits) workgroups
+ * to fill cu_count compute units, without splits shorter than a few granules. cu_count <= 0
+ * means 256 (MI355X). Always returns 1 .. FA8_MAX_SPLITS. */
+int32_t fa8_decode_num_splits(int32_t batch, int32_t heads_kv, int32_t max_seqlen_k, int32_t cu_count);
+
+/* Bytes of o_partial + lse_partial for the given problem (o_partial first, then lse_partial,
+ * each 256-byte aligned), or 0 on overflow. */
+size_t fa8_decode_workspace_bytes(int32_t num_splits, int32_t batch, int32_t max_seqlen_q,
+                                  int32_t heads_q, int32_t dv);
+
+/* Thread-local description of the last non-OK status returned on this thread ("" if none). */
+const char* fa8_last_error(void);
+
+/* Library version string. */
+const char* fa8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA8_H */

@@ -88,7 +88,9 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
         if x is None:
             return 1.0
         a = np.asarray(x, np.float64)
-        return float(a) if a.ndim == 0 else float(a[b, kvh])
+        if a.ndim == 0:
+            return float(a)
+        return float(a[b if a.shape[0] > 1 else 0, kvh if a.shape[1] > 1 else 0])
 
     out = {}
     clipped = 0

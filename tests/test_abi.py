@@ -1,0 +1,160 @@
+"""The C-ABI library loads, exports every entry point include/fa8.h declares, and its host-side
+validation rejects bad arguments before any launch. No GPU is needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from fa8_fwd_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa8.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = binding.load()
+    names = declared_functions()
+    assert {"fa8_fwd_prefill", "fa8_fwd_decode_splitkv", "fa8_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fa8.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.lib_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa8_[a-z0-9_]+)", out))
+    assert set(names) <= exported
+    assert binding.version().startswith("fa8")
+
+
+def test_header_compiles_as_c():
+    src = '#include "fa8.h"\nint main(void){ fa8_fwd_params p; (void)p; return (int)FA8_OK; }\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-x", "c", "-",
+                        "-fsyntax-only"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layout_matches_c():
+    # offsetof of the last field and sizeof, computed by the C compiler from the header
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "fa8.h"\nint main(void){printf("%zu %zu %zu",'
+           ' sizeof(fa8_fwd_params), offsetof(fa8_fwd_params, lse_row_stride), offsetof(fa8_fwd_params, softmax_scale));'
+           'return 0;}\n')
+    exe = "/tmp/fa8_layout_probe"
+    r = subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-x", "c", "-", "-o", exe], input=src,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    size, off_last, off_scale = map(int, subprocess.run([exe], capture_output=True, text=True).stdout.split())
+    assert ctypes.sizeof(binding.FwdParams) == size
+    assert binding.FwdParams.lse_row_stride.offset == off_last
+    assert binding.FwdParams.softmax_scale.offset == off_scale
+
+
+def _cpu(shape, dtype=torch.uint8):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _base(d=128, dv=128, hq=8, hkv=2, sq=16, sk=64, b=2):
+    q = _cpu((b, sq, hq, d))
+    k = _cpu((b, sk, hkv, d))
+    v = _cpu((b, sk, hkv, dv))
+    out = _cpu((b, sq, hq, dv), torch.bfloat16)
+    return q, k, v, out
+
+
+def test_valid_params_ok():
+    q, k, v, out = _base()
+    assert binding.check_params(q, k, v, out=out) == binding.FA8_OK
+    assert binding.check_params(q, k, v, num_splits=4) == binding.FA8_OK
+
+
+@pytest.mark.parametrize("d,dv", [(32, 32), (128, 64), (160, 160), (512, 512), (64, 128)])
+def test_unsupported_head_dims(d, dv):
+    q, k, v, out = _base(d=d, dv=dv)
+    assert binding.check_params(q, k, v, out=out) == binding.FA8_ERR_UNSUPPORTED
+    assert "not supported" in binding.last_error()
+
+
+def test_gqa_ratio_must_divide():
+    q, k, v, out = _base(hq=6, hkv=4)
+    assert binding.check_params(q, k, v, out=out) == binding.FA8_ERR_INVALID
+    assert "multiple" in binding.last_error()
+
+
+def test_bad_num_splits():
+    q, k, v, out = _base()
+    assert binding.check_params(q, k, v, num_splits=binding.MAX_SPLITS + 1) == binding.FA8_ERR_INVALID
+    assert binding.check_params(q, k, v, num_splits=-1) == binding.FA8_ERR_INVALID
+
+
+def test_misaligned_stride_rejected():
+    q = _cpu((2, 16, 8, 144))[..., :128]      # head stride 144 is a multiple of 16: fine
+    k = _cpu((2, 64, 2, 128))
+    v = _cpu((2, 64, 2, 128))
+    out = _cpu((2, 16, 8, 128), torch.bfloat16)
+    assert binding.check_params(q, k, v, out=out) == binding.FA8_OK
+    q2 = _cpu((2, 16, 8, 136))[..., :128]     # head stride 136 is not
+    assert binding.check_params(q2, k, v, out=out) == binding.FA8_ERR_INVALID
+
+
+def test_bad_window_and_dtype():
+    q, k, v, out = _base()
+    assert binding.check_params(q, k, v, out=out, window_left=-2) == binding.FA8_ERR_INVALID
+    with pytest.raises(binding.FA8Error):
+        binding.check_params(q.to(torch.float16), k, v, out=out)     # not E4M3 bytes
+    with pytest.raises(binding.FA8Error):
+        binding.check_params(q, k, v, out=out.to(torch.float32))
+
+
+def test_paged_needs_power_of_two_pages_and_seqused():
+    q = _cpu((4, 1, 8, 128))
+    k = _cpu((10, 12, 2, 128))
+    v = _cpu((10, 12, 2, 128))
+    table = torch.zeros((4, 8), dtype=torch.int32)
+    used = torch.full((4,), 40, dtype=torch.int32)
+    out = _cpu((4, 1, 8, 128), torch.bfloat16)
+    assert binding.check_params(q, k, v, out=out, block_table=table, seqused_k=used) == binding.FA8_ERR_INVALID
+    assert "power of two" in binding.last_error()
+    k = _cpu((10, 16, 2, 128))
+    v = _cpu((10, 16, 2, 128))
+    assert binding.check_params(q, k, v, out=out, block_table=table, seqused_k=used) == binding.FA8_OK
+    assert binding.check_params(q, k, v, out=out, block_table=table) == binding.FA8_ERR_INVALID
+    # a table narrower than max_seqlen_k / page_size
+    assert binding.check_params(q, k, v, out=out, block_table=table, seqused_k=used,
+                                max_seqlen_k=16 * 9) == binding.FA8_ERR_INVALID
+
+
+def test_empty_problem_is_ok():
+    q, k, v, out = _base(b=0)
+    assert binding.check_params(q, k, v, out=out) == binding.FA8_OK
+    q, k, v, out = _base(sq=0)
+    assert binding.check_params(q, k, v, out=out) == binding.FA8_OK
+
+
+def test_null_out_rejected_for_prefill():
+    lib = binding.load()
+    q, k, v, out = _base()
+    p = binding._params(q, k, v, None, None, None, None, None, None, None, None, None, 0.0, False, -1, -1)
+    assert lib.fa8_check_params(ctypes.byref(p), 0) == binding.FA8_ERR_INVALID
+
+
+def test_workspace_bytes():
+    n = binding.decode_workspace_bytes(4, 64, 1, 32, 128)
+    o = 4 * 64 * 32 * 128 * 4
+    l = 4 * 64 * 32 * 4
+    assert n == (-(-o // 256)) * 256 + (-(-l // 256)) * 256
+    assert binding.decode_workspace_bytes(-1, 1, 1, 1, 64) == 0
+
+
+def test_num_splits_heuristic_bounds():
+    for b, h, s in [(1, 1, 1), (64, 8, 8192), (4, 1, 131072), (1, 8, 100), (512, 8, 1024), (1, 1, 1 << 29)]:
+        n = binding.decode_num_splits(b, h, s)
+        assert 1 <= n <= binding.MAX_SPLITS
+    # long single-sequence decode gets many splits; a full batch gets few
+    assert binding.decode_num_splits(4, 1, 131072) >= 64
+    assert binding.decode_num_splits(512, 8, 8192) <= 2

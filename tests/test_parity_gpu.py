@@ -1,0 +1,227 @@
+"""GPU parity: the HIP kernels through the C ABI against the fp64 CPU oracle, element by element,
+at |gpu - ref| <= 2e-2 + 2e-2 |ref| (bf16/fp16 output), LSE within 1e-2."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fa8_fwd_amd import binding
+from fa8_fwd_amd import inputs as gen
+
+from helpers import (check_against_oracle, compare, compare_lse, run_decode, run_prefill, split_key_ranges,
+                     tensors)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, got, glse, what, strict=True, emu=True, num_splits=1):
+    print(check_against_oracle(inp, got, glse, what, strict, emu, num_splits), flush=True)
+
+
+def _prefill_check(inp, what, strict=True, emu=True):
+    got, glse = run_prefill(inp)
+    _check(inp, got, glse, what, strict, emu)
+    return got
+
+
+def test_tiny_config():
+    _prefill_check(gen.tiny(0), "tiny b1 h1 q128 k256 d64")
+
+
+@pytest.mark.parametrize("d,dv", [(64, 64), (96, 96), (128, 128), (192, 192), (256, 256), (192, 128)])
+@pytest.mark.parametrize("mode", ["full", "causal", "window"])
+def test_prefill_head_dims_and_masks(d, dv, mode):
+    causal = mode != "full"
+    wl = 37 if mode == "window" else -1
+    inp = gen.make_dense(100 + d + dv, 2, 203, 331, 4, 2, d, dv, causal=causal, window_left=wl,
+                         descales=(0.5, 0.5, 1.5))
+    # a 38-key window is far narrower than the workloads' (1024): the method's rounding bound applies
+    _prefill_check(inp, f"prefill d{d} dv{dv} {mode} q203 k331", strict=(mode != "window"))
+
+
+@pytest.mark.parametrize("d,dv", [(64, 64), (128, 128), (256, 256)])
+def test_prefill_peaked_softmax_within_method_bound(d, dv):
+    # per-(b, kv_head) descales up to 2 on q and k make the softmax far sharper than the
+    # workloads' (few hundred keys); the method's E4M3 P rounding then bounds the error
+    inp = gen.make_dense(100 + d + dv, 2, 203, 331, 4, 2, d, dv, descales=(("uniform", 0.5, 2.0),) * 3)
+    _prefill_check(inp, f"prefill peaked d{d}", strict=False)
+
+
+def test_prefill_causal_gqa_ragged():
+    # several row blocks, ragged tail, Sq < Sk (bottom-right), GQA 8:1, scalar descales
+    inp = gen.make_dense(5, 2, 300, 517, 16, 2, 128, 128, causal=True, descales=(0.5, 0.5, 1.5))
+    _prefill_check(inp, "prefill causal q300 k517 gqa8")
+
+
+def test_prefill_sq_longer_than_sk_has_empty_rows():
+    inp = gen.make_dense(6, 1, 150, 70, 2, 1, 128, 128, causal=True)
+    got = _prefill_check(inp, "empty rows", strict=False)   # rows 80.. see 1..70 keys
+    _, glse = run_prefill(inp)
+    assert np.all(got[0, :80] == 0) and np.all(np.isneginf(glse[0, :, :80]))
+
+
+def test_prefill_varlen_window_fp16():
+    inp = gen.mixed_varlen(4, d=256, dv=256, nseq=4, lo=64, hi=700, window=128)
+    # 128-key windows and causal starts of sequences: few keys per row, the method's bound applies
+    _prefill_check(inp, "varlen d256 window128 fp16", strict=False)
+    inp = gen.mixed_varlen(4, d=192, dv=128, nseq=4, lo=64, hi=700, window=128)
+    _prefill_check(inp, "varlen d192/128 window128 fp16", strict=False)
+
+
+def test_prefill_varlen_empty_rows():
+    inp = gen.mixed_varlen(9, d=128, dv=128, nseq=5, lo=30, hi=300, window=64, allow_empty_rows=True)
+    _prefill_check(inp, "varlen with Sq > Sk rows", strict=False)
+
+
+def test_prefill_paged_equals_contiguous_bitwise():
+    inp = gen.make_paged(7, [300, 17, 640, 129], 8, 2, 128, 128, page_size=16, sq=40, varlen_q=False, causal=True)
+    got, glse = run_prefill(inp)
+    _check(inp, got, glse, "paged prefill", strict=False)   # a 17-key sequence
+    # same tokens, contiguous varlen K/V
+    sk = inp.seqused_k.astype(np.int64)
+    ks, vs = [], []
+    for b in range(inp.batch):
+        j = np.arange(sk[b])
+        pg = inp.block_table[b, j // 16]
+        ks.append(inp.k[pg, j % 16])
+        vs.append(inp.v[pg, j % 16])
+    cont = gen.make_dense(7, 4, 40, 1, 8, 2, 128, 128, causal=True)
+    cont.q = inp.q
+    cont.k, cont.v = np.concatenate(ks), np.concatenate(vs)
+    cont.cu_seqlens_k = np.concatenate([[0], np.cumsum(sk)]).astype(np.int32)
+    cont.max_seqlen_k = int(sk.max())
+    got2, glse2 = run_prefill(cont)
+    assert np.array_equal(got, got2) and np.array_equal(glse, glse2)
+
+
+def test_prefill_deterministic():
+    inp = gen.make_dense(8, 1, 256, 256, 4, 4, 128, 128, causal=True)
+    a, la = run_prefill(inp)
+    b, lb = run_prefill(inp)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("mode", ["omitted", "scalar", "per_bh", "broadcast_b"])
+def test_descale_modes(mode):
+    inp = gen.make_dense(9, 3, 70, 150, 4, 2, 128, 128, causal=True)
+    rng = np.random.default_rng(0)
+    if mode == "scalar":
+        inp.q_descale, inp.k_descale, inp.v_descale = (np.array(x, np.float32) for x in (0.7, 1.3, 2.0))
+    elif mode == "per_bh":
+        inp.q_descale, inp.k_descale, inp.v_descale = (rng.uniform(0.5, 2, (3, 2)).astype(np.float32) for _ in range(3))
+    elif mode == "broadcast_b":
+        # (1, Hkv) descales broadcast over the batch without a copy
+        dq = rng.uniform(0.5, 2, (1, 2)).astype(np.float32)
+        inp.q_descale = dq
+    got, glse = run_prefill(inp)
+    _check(inp, got, glse, f"descales {mode}", strict=False)
+
+
+def _decode_check(inp, num_splits, what, strict=True, emu=True):
+    got, glse = run_decode(inp, num_splits)
+    # the emulator splits the same 64-key granules as the kernel when the rows see [0, Sk)
+    ns = 1 if (num_splits is None or inp.window_left >= 0) else num_splits
+    _check(inp, got, glse, what, strict, emu and num_splits is not None and inp.window_left < 0, ns)
+    return got
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, None])
+def test_decode_paged_gqa(num_splits):
+    # the paged GQA decode workload at batch 8: lengths 1k-4k, per-(b, kv_head) descales
+    inp = gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096)
+    _decode_check(inp, num_splits, f"paged decode b8 splits={num_splits}")
+
+
+def test_decode_short_sequences_peaked():
+    inp = gen.paged_gqa_decode(2, batch=8, lo=1, hi=400)
+    _decode_check(inp, 3, "paged decode short peaked", strict=False)
+
+
+@pytest.mark.parametrize("sq,page", [(4, 16), (4, 64), (2, 64)])
+@pytest.mark.parametrize("causal,wl", [(True, -1), (True, 100), (False, -1)])
+def test_decode_multi_token(sq, page, causal, wl):
+    sk = [300, 1000, 64, 1]
+    inp = gen.make_paged(10 + sq, sk, 8, 2, 128, 128, page_size=page, sq=sq, varlen_q=True, causal=causal,
+                         window_left=wl, descales=(("uniform", 0.5, 2.0),) * 3)
+    _decode_check(inp, 4, f"decode sq{sq} page{page} causal{causal} wl{wl}", strict=False)
+
+
+@pytest.mark.parametrize("d,dv", [(64, 64), (96, 96), (192, 192), (256, 256), (192, 128)])
+def test_decode_head_dims(d, dv):
+    inp = gen.make_paged(20 + d, [500, 77, 1200], 16, 4, d, dv, page_size=16, sq=1, varlen_q=True)
+    _decode_check(inp, 2, f"decode d{d} dv{dv}")
+
+
+def test_decode_partials_match_oracle_ranges():
+    # partial LSEs use the same rounded-P sums as the final LSE: few keys per split, method bound
+    inp = gen.make_paged(30, [700, 1500, 90], 8, 2, 128, 128, page_size=16, sq=2, varlen_q=True, causal=True)
+    S = 5
+    q, k, v, kw = tensors(inp)
+    op, lp = binding.decode_splitkv(q, k, v, num_splits=S, **kw)
+    torch.cuda.synchronize()
+    op, lp = op.cpu().numpy(), lp.cpu().numpy()
+    rows, ranges = split_key_ranges(inp, S)
+    rb, rh, ri = rows
+    for s in range(S):
+        ro, rl = oracle.attention(inp, rows=rows, key_range=ranges[s])
+        go = op[s, rb, ri, rh]
+        gl = lp[s, rb, ri, rh]
+        compare(go, ro, f"partial split {s}")
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(gl), fin)
+        assert np.abs(gl[fin] - rl[fin]).max() <= 0.0646, f"partial lse split {s}"
+
+
+def test_decode_empty_and_poisoned_pages():
+    # a zero-length sequence and NaN-filled unused pages / tail slots must not reach the output
+    inp = gen.make_paged(31, [0, 33, 200, 16], 8, 2, 128, 128, page_size=16, sq=1, varlen_q=True)
+    used = set()
+    for b, s in enumerate(inp.seqused_k):
+        used.update(inp.block_table[b, : (int(s) + 15) // 16].tolist())
+    for pg in range(inp.k.shape[0]):
+        if pg not in used:
+            inp.k[pg] = 0x7F
+            inp.v[pg] = 0x7F
+    for b, s in enumerate(inp.seqused_k):
+        s = int(s)
+        if s % 16:
+            pg = inp.block_table[b, s // 16]
+            inp.k[pg, s % 16:] = 0x7F
+            inp.v[pg, s % 16:] = 0x7F
+    got = _decode_check(inp, 3, "decode with poison")
+    assert np.all(got[0] == 0)
+
+
+def test_long_kv_no_shrinkage():
+    # V ~ N(0.5, 1), one split and many: error relative to the fp64 RMS stays at the FP8 level
+    inp = gen.long_kv_decode(3, batch=2, seqlen=32768, page_size=64)
+    ref, _ = oracle.attention_full(inp)
+    for S in (1, 64):
+        got, _ = run_decode(inp, S)
+        err, rel = compare(got, ref, f"long kv splits={S}")
+        ratio = got.mean() / ref.mean()
+        print(f"long kv 32k splits={S}: rel-RMS {rel * 100:.3f}% mean ratio {ratio:.5f}", flush=True)
+        assert rel < 0.01
+        assert 0.99 <= ratio <= 1.01
+
+
+def test_combine_entry_point_alone():
+    # random partials with some empty splits, combined on the GPU vs the oracle's combine
+    rng = np.random.default_rng(1)
+    S, B, SQ, HQ, DV = 6, 3, 2, 4, 128
+    op = rng.standard_normal((S, B, SQ, HQ, DV)).astype(np.float32)
+    lp = (rng.standard_normal((S, B, SQ, HQ)) * 3).astype(np.float32)
+    lp[1] = -np.inf
+    lp[:, 2, 1, 3] = -np.inf          # one row with every split empty
+    ref_o, ref_l = oracle.combine(op, lp)
+    ref_o[2, 1, 3] = 0
+    dev = torch.device("cuda:0")
+    out = torch.empty((B, SQ, HQ, DV), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, HQ, SQ), dtype=torch.float32, device=dev)
+    binding.combine(torch.from_numpy(op).to(dev), torch.from_numpy(lp).to(dev), batch=B, max_seqlen_q=SQ,
+                    heads_q=HQ, dv=DV, out=out, lse=lse)
+    torch.cuda.synchronize()
+    compare(out.float().cpu().numpy(), ref_o, "combine")
+    compare_lse(lse.cpu().numpy(), ref_l.transpose(0, 2, 1), "combine lse")
