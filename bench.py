@@ -1,0 +1,293 @@
+"""Benchmark of the FP8 attention forward on one MI355X.
+
+One step = one split-KV decode pass plus its combine over the paged GQA decode workload
+(64 sequences, 32 query / 8 KV heads, d = 128, one query token, 16-token pages, lengths
+uniform in [1024, 8192], per-(batch, kv head) descales): the headline value is its whole-step
+K+V bandwidth in GB/s. The causal-prefill workload (B = 2, 8192 x 8192, 32/8 heads, d = 128)
+is timed next to it and reported in TFLOP/s under "prefill".
+
+Prints one JSON line. Inputs are resident in HBM before timing; the dominant kernel's own
+duration is measured with HIP events on its launch stream over the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+import torch
+
+from fa8_fwd_amd import binding
+from fa8_fwd_amd import inputs as gen
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
+
+
+# ---------------------------------------------------------------------------------------------
+# work counts (algorithmic: what the method must read/write/compute, not what a kernel wastes)
+# ---------------------------------------------------------------------------------------------
+
+def visible_pairs(inp) -> int:
+    """(query, key) pairs visible under the causal/window mask, summed over batches."""
+    sq, sk = inp.seqlens_q(), inp.seqlens_k()
+    total = 0
+    wr = 0 if inp.causal else inp.window_right
+    for b in range(inp.batch):
+        i = np.arange(int(sq[b]), dtype=np.int64)
+        ip = i + int(sk[b]) - int(sq[b])
+        hi = np.full_like(i, int(sk[b]))
+        if wr >= 0:
+            hi = np.minimum(hi, ip + wr + 1)
+        lo = np.zeros_like(i)
+        if inp.window_left >= 0:
+            lo = np.maximum(lo, ip - inp.window_left)
+        total += int(np.clip(hi - lo, 0, None).sum())
+    return total
+
+
+def prefill_flop(inp) -> int:
+    """2 * (d + dv) FLOP per visible pair and query head (QK^T and PV)."""
+    return visible_pairs(inp) * inp.heads_q * 2 * (inp.d + inp.dv)
+
+
+def decode_kernel_bytes(inp) -> int:
+    """Bytes the split-KV decode kernel must move: every visible K and V row once
+    (sum_b s_b * Hkv * (d + dv)), the Q rows, the block-table entries and lengths, the descales."""
+    sk = inp.seqlens_k()
+    sq = inp.seqlens_q()
+    kv = int(sk.sum()) * inp.heads_kv * (inp.d + inp.dv)
+    q = int(sq.sum()) * inp.heads_q * inp.d
+    table = int(((sk + inp.page_size - 1) // inp.page_size).sum()) * 4 if inp.block_table is not None else 0
+    lens = inp.batch * 4 * 2
+    desc = sum(0 if x is None else x.size * 4 for x in (inp.q_descale, inp.k_descale, inp.v_descale))
+    return kv + q + table + lens + desc
+
+
+def decode_step_bytes(inp) -> int:
+    """Whole decode step: the kernel's bytes plus the bf16 output written once."""
+    return decode_kernel_bytes(inp) + int(inp.seqlens_q().sum()) * inp.heads_q * inp.dv * 2
+
+
+# ---------------------------------------------------------------------------------------------
+
+def to_dev(x, dev):
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def device_args(inp, dev):
+    kw = dict(cu_seqlens_q=to_dev(inp.cu_seqlens_q, dev), cu_seqlens_k=to_dev(inp.cu_seqlens_k, dev),
+              seqused_k=to_dev(inp.seqused_k, dev), block_table=to_dev(inp.block_table, dev),
+              max_seqlen_q=inp.max_seqlen_q, max_seqlen_k=inp.max_seqlen_k,
+              q_descale=to_dev(inp.q_descale, dev), k_descale=to_dev(inp.k_descale, dev),
+              v_descale=to_dev(inp.v_descale, dev), softmax_scale=inp.softmax_scale, causal=inp.causal,
+              window_left=inp.window_left, window_right=inp.window_right)
+    return to_dev(inp.q, dev), to_dev(inp.k, dev), to_dev(inp.v, dev), kw
+
+
+def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None):
+    q, k, v, kw = device_args(inp, dev)
+    B, HQ, SQ, DV = inp.batch, inp.heads_q, inp.max_seqlen_q, inp.dv
+    S = num_splits or binding.decode_num_splits(B, inp.heads_kv, inp.max_seqlen_k)
+    op = torch.empty((S, B, SQ, HQ, DV), dtype=torch.float32, device=dev)
+    lp = torch.empty((S, B, SQ, HQ), dtype=torch.float32, device=dev)
+    out = torch.empty((q.shape[0], HQ, DV), dtype=torch.bfloat16, device=dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        binding.decode_splitkv(q, k, v, num_splits=S, o_partial=op, lse_partial=lp, **kw)
+        if evs is not None:
+            evs[1].record()
+        binding.combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=kw["cu_seqlens_q"])
+
+    for _ in range(warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    return (t1 - t0) * 1e3 / steps, kernel_ms, S
+
+
+def bench_prefill(inp, steps: int, warmup: int, dev):
+    q, k, v, kw = device_args(inp, dev)
+    out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        binding.prefill(q, k, v, out=out, **kw)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        binding.prefill(q, k, v, out=out, **kw)
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    return (t1 - t0) * 1e3 / steps, kernel_ms
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_decode(inp, budget_s: float):
+    """The oracle (fp64 C, OpenMP on the host cores) on a bounded sample of the decode workload:
+    all query heads of the first few sequences, grown until about budget_s of CPU time."""
+    import oracle
+    cores = host_cores()
+    oracle.attention(inp, rows=(np.zeros(1, np.int32), np.zeros(1, np.int32), np.zeros(1, np.int32)), threads=cores)
+    rb_all, rh_all, ri_all = oracle.all_rows(inp)
+    sk = inp.seqlens_k()
+    nb, elapsed, reps = 1, 0.0, 1
+    while True:
+        sel = rb_all < nb
+        t0 = time.perf_counter()
+        oracle.attention(inp, rows=(rb_all[sel], rh_all[sel], ri_all[sel]), threads=cores)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s / 3 or nb >= inp.batch:
+            break
+        nb = min(inp.batch, max(nb + 1, int(nb * min(8.0, budget_s / 3 / max(elapsed, 1e-3)))))
+    if nb >= inp.batch and elapsed < budget_s / 2:
+        # the whole workload is quicker than the budget: repeat it for a steadier rate
+        reps = max(1, int(budget_s / 2 / max(elapsed, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.attention(inp, rows=(rb_all, rh_all, ri_all), threads=cores)
+        elapsed = (time.perf_counter() - t0) / reps
+    # bytes of the sampled sequences, as counted for the GPU step
+    kv = int(sk[:nb].sum()) * inp.heads_kv * (inp.d + inp.dv)
+    frac = nb / inp.batch
+    nbytes = kv + frac * (decode_step_bytes(inp) - int(sk.sum()) * inp.heads_kv * (inp.d + inp.dv))
+    return {"value": round(nbytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nb} of {inp.batch} sequences (all {inp.heads_q} query heads), {elapsed:.2f} s per pass "
+                      f"(mean of {reps}) on {cores} threads of {cpu_model()}"}
+
+
+def cpu_baseline_prefill(inp, budget_s: float):
+    """The oracle on every `stride`-th query row of every (batch, head) of the causal prefill
+    workload, scaled by the visible pairs it covered."""
+    import oracle
+    cores = host_cores()
+    rb_all, rh_all, ri_all = oracle.all_rows(inp)
+    stride = 4096
+    while True:
+        sel = (ri_all % stride) == (stride - 1)
+        rows = (rb_all[sel], rh_all[sel], ri_all[sel])
+        t0 = time.perf_counter()
+        oracle.attention(inp, rows=rows, threads=cores)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s / 3 or stride <= 8:
+            break
+        stride = max(8, int(stride / min(8.0, budget_s / 3 / max(elapsed, 1e-3))))
+    # visible keys of the sampled rows (causal, Sq == Sk): i + 1
+    pairs = int((rows[2].astype(np.int64) + 1).sum())
+    flop = pairs * 2 * (inp.d + inp.dv)
+    return {"value": round(flop / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"every {stride}th query row of all heads ({len(rows[0])} rows), {elapsed:.1f} s on {cores} "
+                      f"threads of {cpu_model()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time per workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this FP8 attention forward has no multi-GPU path "
+              "(each GPU would run the same kernels on its own share of heads or pages)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    binding.load()
+
+    dec = gen.paged_gqa_decode(1)
+    ms_step, kern_ms, S = bench_decode(dec, args.steps, args.warmup, dev, args.num_splits or None)
+    step_bytes = decode_step_bytes(dec)
+    kbytes = decode_kernel_bytes(dec)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kbytes / (kern_ms * 1e-3) / 1e9
+    line = {
+        "metric": "FP8 attn fwd TFLOP/s (prefill) & decode HBM GB/s, % of MI355X peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": dec.name, "batch": dec.batch, "heads_q": dec.heads_q, "heads_kv": dec.heads_kv,
+                   "d": dec.d, "page_size": dec.page_size, "seqlens_k": "uniform [1024, 8192], seed 1",
+                   "sum_seqlen_k": int(dec.seqlens_k().sum()), "num_splits": S, "out": "bf16",
+                   "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "roofline": {"bound": "hbm", "kernel": "fa8_attn_kernel<128,128,1,true> (split-KV decode)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms": round(kern_ms, 5), "bytes_per_launch": kbytes},
+    }
+    if not args.no_prefill:
+        pre = gen.causal_prefill(2)
+        p_ms, p_kern = bench_prefill(pre, args.prefill_steps, max(2, args.warmup // 5), dev)
+        flop = prefill_flop(pre)
+        tfl = flop / (p_ms * 1e-3) / 1e12
+        ktfl = flop / (p_kern * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": pre.name, "value": round(tfl, 2), "unit": "TFLOP/s", "ms_per_step": round(p_ms, 4),
+            "steps": args.prefill_steps, "flop_per_step": flop, "pct_of_fp8_peak": round(100 * tfl / FP8_PEAK_TFLOPS, 2),
+            "roofline": {"bound": "mfma", "kernel": "fa8_attn_kernel<128,128,4,false> (prefill)",
+                         "achieved": round(ktfl, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ktfl / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel_ms": round(p_kern, 4)},
+        }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
+        if "prefill" in line:
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(gen.causal_prefill(2), args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
