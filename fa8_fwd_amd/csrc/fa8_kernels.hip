@@ -1,8 +1,9 @@
 // gfx950 (MI355X) kernels of the FP8 attention forward.
 //
-// One kernel template serves the full forward pass (one query head per workgroup, 128 query
-// rows) and the split-KV decode pass (the q heads of one KV head packed into 32 rows). Per KV
-// tile of 64 keys, each wave of 32 query rows does:
+// Two kernels share one per-tile routine (attn_tile): the full forward pass (fa8_prefill_kernel,
+// four waves and 128 query rows of one query head per workgroup) and the split-KV decode pass
+// (fa8_decode_kernel, one wave per workgroup, the q heads of one KV head packed as 32 rows).
+// Per KV tile, each wave of 32 query rows does:
 //   S^T = K Q^T          FP8 MFMA 32x32x64 (E4M3 x E4M3 -> fp32); rows = keys, cols = queries,
 //                        so one lane owns one query row (the page's "QK^T" step)
 //   scale, mask          x = S * c, c = softmax_scale * dq * dk * log2(e)  (q/k descales folded
@@ -13,11 +14,11 @@
 //   P = exp2(x - m + 8)  one FMA feeds v_exp_f32 (the fused exp2 bias; 2^8 pre-scale of P:
 //                        Design, "P in FP8"); P cast to E4M3 (RNE); row sum l in fp32 over
 //                        the rounded P, the values the PV product actually uses
-//   O_t = V^T P^T        FP8 MFMA from zero for this tile only, then O = alpha*O + O_t in fp32
+//   O_t = V^T P^T        FP8 MFMA from zero over this tile only, then O = alpha*O + O_t in fp32
 //                        (Design, "Two-level PV accumulation")
 // and at the end O *= dv / l, LSE = ln2 * (m + log2 l - 8) (bias removed from the LSE).
 //
-// Layout choices for gfx950 (measured MFMA lane layouts; see the design notes):
+// Layout choices for gfx950 (from measured MFMA lane layouts):
 //  * MFMA operands: lane L holds row L%32 of A (col L%32 of B) and 32 bytes of the contraction
 //    dimension, lanes 0-31 one half and 32-63 the other; A and B use the same byte<->k order, so
 //    any k permutation applied to both operands leaves the product unchanged.
@@ -26,7 +27,7 @@
 //    PV MFMA; the A operand (V^T) is read with the same key permutation by ds_read_b64_tr_b8
 //    from the row-major V tile (no separate transpose pass over V).
 //  * K and V tiles are row-major in LDS with a per-row XOR swizzle of their 16-byte chunks so
-//    the 32 row reads of an operand hit distinct banks.
+//    the rows that one LDS read instruction touches fall in distinct banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,8 +55,16 @@ __device__ __forceinline__ v16f mfma_32x32x64_fp8(v8i a, v8i b, v16f c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Position of 16-byte chunk `ch` of a row holding NCH chunks, XOR-swizzled by `sv` inside the
-// largest aligned power-of-two group of chunks that fits in the row.
+// largest aligned power-of-two group of chunks that fits in the row (an involution).
 template <int NCH>
 __device__ __forceinline__ int swz(int ch, int sv) {
   if ((ch | 7) < NCH) return ch ^ (sv & 7);
@@ -99,304 +108,194 @@ __device__ __forceinline__ float load_descale(const float* p, int64_t sb, int64_
   return p ? p[(int64_t)b * sb + (int64_t)kvh * sh] : 1.0f;
 }
 
-template <int D, int DV, int NW, bool PACKED>
-__global__ void __launch_bounds__(NW * 64)
-fa8_attn_kernel(const KParams p) {
-  constexpr int BN = kKvTile;
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32;
-  constexpr int KS = (D + 63) / 64;       // k-steps of the QK MFMA (d padded to 64)
-  constexpr int NB = DV / 32;             // 32-wide dv blocks of the PV MFMA
+// Key-position ranges of one query row, bottom-right aligned.
+struct RowRange {
+  int sk, shift, wl, wr;
+  __device__ int lo(int i) const { return wl >= 0 ? max(0, i + shift - wl) : 0; }
+  __device__ int hi(int i) const { return wr >= 0 ? min(sk, i + shift + wr + 1) : sk; }
+};
+
+// Sequence lengths of batch b.
+struct SeqInfo {
+  int q0, sq, sk;
+};
+__device__ __forceinline__ SeqInfo seq_info(const KParams& p, int b) {
+  SeqInfo s;
+  s.q0 = p.cu_q ? p.cu_q[b] : 0;
+  s.sq = p.cu_q ? p.cu_q[b + 1] - s.q0 : p.max_sq;
+  if (p.used_k) s.sk = p.used_k[b];
+  else if (p.cu_k) s.sk = p.cu_k[b + 1] - p.cu_k[b];
+  else s.sk = p.max_sk;
+  return s;
+}
+
+// Element offsets of K/V row j of (batch b, kv head kvh).
+struct KvAddr {
+  const int32_t* trow;   // block-table row, or null
+  int64_t kbase, vbase;  // offset of key 0 (non-paged) or of the kv head within a page (paged)
+  int64_t k_ps, v_ps, k_rs, v_rs;
+  int shift, pmask;
+  __device__ int64_t k(int j) const {
+    if (trow) return (int64_t)trow[j >> shift] * k_ps + (int64_t)(j & pmask) * k_rs + kbase;
+    return kbase + (int64_t)j * k_rs;
+  }
+  __device__ int64_t v(int j) const {
+    if (trow) return (int64_t)trow[j >> shift] * v_ps + (int64_t)(j & pmask) * v_rs + vbase;
+    return vbase + (int64_t)j * v_rs;
+  }
+};
+__device__ __forceinline__ KvAddr kv_addr(const KParams& p, int b, int kvh) {
+  KvAddr a;
+  const bool paged = p.page_shift >= 0;
+  a.trow = paged ? p.table + (int64_t)b * p.table_stride : nullptr;
+  a.kbase = paged ? (int64_t)kvh * p.k_hs
+                  : (p.cu_k ? (int64_t)p.cu_k[b] * p.k_rs : (int64_t)b * p.k_bs) + (int64_t)kvh * p.k_hs;
+  a.vbase = paged ? (int64_t)kvh * p.v_hs
+                  : (p.cu_k ? (int64_t)p.cu_k[b] * p.v_rs : (int64_t)b * p.v_bs) + (int64_t)kvh * p.v_hs;
+  a.k_ps = p.k_bs;
+  a.v_ps = p.v_bs;
+  a.k_rs = p.k_rs;
+  a.v_rs = p.v_rs;
+  a.shift = paged ? p.page_shift : 0;
+  a.pmask = paged ? (1 << p.page_shift) - 1 : 0;
+  return a;
+}
+
+// Q row of this lane as the B operand of S^T = K Q^T: d-bytes [64ks + 32*hgrp, +32).
+template <int D>
+__device__ __forceinline__ void load_q(const uint8_t* qrow, bool valid, int hgrp, v8i (&qop)[(D + 63) / 64]) {
+#pragma unroll
+  for (int ks = 0; ks < (D + 63) / 64; ks++) {
+    const int off = ks * 64 + hgrp * 32;
+    v4i a = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+    if (valid && off < D) {
+      a = ld_global16(qrow + off);
+      a2 = ld_global16(qrow + off + 16);
+    }
+    qop[ks] = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+  }
+}
+
+// One KV tile of BN keys (LDS K tile at kt, V tile at vt, both row-major and swizzled) for the
+// 32 query rows of this wave. Updates the running max m, row sum l and O accumulators.
+template <int D, int DV, int BN>
+__device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_LDS uint8_t* vt,
+                                          const v8i (&qop)[(D + 63) / 64], float c, bool need_mask, int j0,
+                                          int my_lo, int my_hi, int lane, float& m_run, float& l_run,
+                                          v16f (&oacc)[DV / 32]) {
+  constexpr int KB = BN / 32;        // 32-key blocks of S^T
+  constexpr int PK = BN / 64;        // 64-key k-steps of PV
+  constexpr int KS = (D + 63) / 64;  // k-steps of QK
+  constexpr int NB = DV / 32;
   constexpr int KCH = D / 16, VCH = DV / 16;
-  constexpr int KTILE = BN * D, VTILE = BN * DV, STAGE = KTILE + VTILE;
-  constexpr int KCHUNKS = BN * KCH, VCHUNKS = BN * VCH;
-  constexpr int KPT = (KCHUNKS + NT - 1) / NT, VPT = (VCHUNKS + NT - 1) / NT;
-  static_assert(DV % 32 == 0 && D % 32 == 0, "head dims must be multiples of 32");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int hgrp = lane >> 5, lrow = lane & 31;
-  const int b = blockIdx.z;
-  const int g = p.g;
 
-  int kvh, mblock, split = 0, hq_fixed = 0;
-  if constexpr (PACKED) {
-    kvh = blockIdx.x / p.nmb;
-    mblock = blockIdx.x - kvh * p.nmb;
-    split = blockIdx.y;
-  } else {
-    hq_fixed = blockIdx.y;
-    kvh = hq_fixed / g;
-    // causal: heaviest (last) row blocks first
-    mblock = p.causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
-  }
-
-  const int q0 = p.cu_q ? p.cu_q[b] : 0;
-  const int sq = p.cu_q ? p.cu_q[b + 1] - q0 : p.max_sq;
-  int sk;
-  if (p.used_k) sk = p.used_k[b];
-  else if (p.cu_k) sk = p.cu_k[b + 1] - p.cu_k[b];
-  else sk = p.max_sk;
-
-  const int rows_total = PACKED ? sq * g : sq;
-  const int rb0 = mblock * BM;
-  if (rb0 >= rows_total) return;               // uniform: no valid row in this block
-  const int rb1 = min(rb0 + BM, rows_total) - 1;
-  const int i_first = PACKED ? rb0 / g : rb0;
-  const int i_last = PACKED ? rb1 / g : rb1;
-
-  const int shift = sk - sq;                   // bottom-right alignment: i' = i + sk - sq
-  auto lo_of = [&](int i) { return p.wl >= 0 ? max(0, i + shift - p.wl) : 0; };
-  auto hi_of = [&](int i) { return p.wr >= 0 ? min(sk, i + shift + p.wr + 1) : sk; };
-
-  int wg_lo = lo_of(i_first), wg_hi = hi_of(i_last);       // union of the rows' key ranges
-  int full_lo = lo_of(i_last), full_hi = hi_of(i_first);   // keys visible to every row
-  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
-  if constexpr (PACKED) {
-    // split s covers granules [g0 + s*n/S, g0 + (s+1)*n/S) of the block's granule range
-    const int g0 = wg_lo / BN, g1 = (wg_hi + BN - 1) / BN, n = g1 - g0;
-    const int s0 = g0 + (int)(((int64_t)split * n) / p.nsplit);
-    const int s1 = g0 + (int)(((int64_t)(split + 1) * n) / p.nsplit);
-    wg_lo = max(wg_lo, s0 * BN);
-    wg_hi = min(wg_hi, s1 * BN);
-    full_lo = max(full_lo, s0 * BN);
-    full_hi = min(full_hi, s1 * BN);
-  }
-  const int t_begin = wg_lo / BN;
-  const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
-
-  // this lane's query row
-  const int ridx = rb0 + wave * 32 + lrow;
-  const bool valid = ridx <= rb1;
-  const int qi = PACKED ? ridx / g : ridx;
-  const int qh = PACKED ? kvh * g + (ridx - qi * g) : hq_fixed;
-  int my_lo = 0, my_hi = 0;
-  if (valid) {
-    my_lo = max(lo_of(qi), wg_lo);
-    my_hi = min(hi_of(qi), wg_hi);
-  }
-
-  const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
-  const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
-  const float dvs = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh);
-  const float c = p.scale_log2 * dq * dk;
-
-  // Q rows as the B operand of S^T = K Q^T: lane holds d-bytes [64ks + 32*hgrp, +32)
-  v8i qop[KS];
-  {
-    const uint8_t* qrow = p.q + (p.cu_q ? (int64_t)(q0 + qi) * p.q_rs : (int64_t)b * p.q_bs + (int64_t)qi * p.q_rs) +
-                          (int64_t)qh * p.q_hs;
+  // ---- S^T = K Q^T ----
+  v16f sacc[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; kb++) {
+#pragma unroll
+    for (int r = 0; r < 16; r++) sacc[kb][r] = 0.0f;
+    const int row = kb * 32 + lrow;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
       const int off = ks * 64 + hgrp * 32;
-      v4i a = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
-      if (valid && off < D) {
-        a = ld_global16(qrow + off);
-        a2 = ld_global16(qrow + off + 16);
+      v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (off < D) {
+        const int ch = off >> 4;
+        const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch, k_sv(row)) * 16);
+        const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch + 1, k_sv(row)) * 16);
+        kop = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
       }
-      qop[ks] = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+      sacc[kb] = mfma_32x32x64_fp8(kop, qop[ks], sacc[kb]);
     }
   }
 
-  // K/V row addressing
-  const bool paged = p.page_shift >= 0;
-  const int32_t* trow = paged ? p.table + (int64_t)b * p.table_stride : nullptr;
-  const int64_t kbase = paged ? (int64_t)kvh * p.k_hs
-                              : (p.cu_k ? (int64_t)p.cu_k[b] * p.k_rs : (int64_t)b * p.k_bs) + (int64_t)kvh * p.k_hs;
-  const int64_t vbase = paged ? (int64_t)kvh * p.v_hs
-                              : (p.cu_k ? (int64_t)p.cu_k[b] * p.v_rs : (int64_t)b * p.v_bs) + (int64_t)kvh * p.v_hs;
-  const int pmask = paged ? (1 << p.page_shift) - 1 : 0;
-  auto koff = [&](int j) -> int64_t {
-    if (paged) {
-      const int64_t page = trow[j >> p.page_shift];
-      return page * p.k_bs + (int64_t)(j & pmask) * p.k_rs + kbase;
-    }
-    return kbase + (int64_t)j * p.k_rs;
-  };
-  auto voff = [&](int j) -> int64_t {
-    if (paged) {
-      const int64_t page = trow[j >> p.page_shift];
-      return page * p.v_bs + (int64_t)(j & pmask) * p.v_rs + vbase;
-    }
-    return vbase + (int64_t)j * p.v_rs;
-  };
-
-  v4i kreg[KPT], vreg[VPT];
-  auto gload = [&](int t) {
-    const int j0 = t * BN;
+  // ---- mask (only tiles that cross some row's key bounds) ----
+  if (need_mask) {
 #pragma unroll
-    for (int u = 0; u < KPT; u++) {
-      const int cidx = tid + u * NT;
-      v4i x = {0, 0, 0, 0};
-      if (KCHUNKS % NT == 0 || cidx < KCHUNKS) {
-        const int row = cidx / KCH, ch = cidx - row * KCH;
-        const int j = j0 + row;
-        if (j < sk) x = ld_global16(p.k + koff(j) + ch * 16);
+    for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hgrp + (r & 3);
+        if (j < my_lo || j >= my_hi) sacc[kb][r] = kNegInf;
       }
-      kreg[u] = x;
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; u++) {
-      const int cidx = tid + u * NT;
-      v4i x = {0, 0, 0, 0};
-      if (VCHUNKS % NT == 0 || cidx < VCHUNKS) {
-        const int row = cidx / VCH, ch = cidx - row * VCH;
-        const int j = j0 + row;
-        if (j < sk) x = ld_global16(p.v + voff(j) + ch * 16);
-      }
-      vreg[u] = x;
-    }
-  };
-  auto swrite = [&](int stage) {
-    uint8_t* kt = smem + stage * STAGE;
-    uint8_t* vt = kt + KTILE;
-#pragma unroll
-    for (int u = 0; u < KPT; u++) {
-      const int cidx = tid + u * NT;
-      if (KCHUNKS % NT == 0 || cidx < KCHUNKS) {
-        const int row = cidx / KCH, ch = cidx - row * KCH;
-        *reinterpret_cast<v4i*>(kt + row * D + swz<KCH>(ch, k_sv(row)) * 16) = kreg[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; u++) {
-      const int cidx = tid + u * NT;
-      if (VCHUNKS % NT == 0 || cidx < VCHUNKS) {
-        const int row = cidx / VCH, ch = cidx - row * VCH;
-        *reinterpret_cast<v4i*>(vt + row * DV + swz<VCH>(ch, v_sv(row)) * 16) = vreg[u];
-      }
-    }
-  };
-
-  // running softmax state of this lane's row (shared by lanes L and L^32)
-  float m_run = kNegInf, l_run = 0.0f;
-  v16f oacc[NB];
-#pragma unroll
-  for (int n = 0; n < NB; n++)
-#pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = 0.0f;
-
-  // per-lane constant of the transposed V read: key offset within a 16-key group
-  const int trj = (lane & 15) >> 1;
-  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
-  const int tr_chunk_hi = (lane >> 4) & 1;
-  const int tr_byte = 8 * (lane & 1);
-
-  if (t_begin < t_end) {
-    gload(t_begin);
-    swrite(0);
-    __syncthreads();
   }
-  for (int t = t_begin; t < t_end; t++) {
-    const int st = (t - t_begin) & 1;
-    if (t + 1 < t_end) gload(t + 1);
-    const uint8_t* kt = smem + st * STAGE;
-    const uint8_t* vt = kt + KTILE;
-    const int j0 = t * BN;
 
-    // ---- S^T = K Q^T ----
-    v16f sacc[2];
+  // ---- row max (lanes L and L^32 share a row), lazy rescale ----
+  float mx = kNegInf;
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
+  for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) sacc[kb][r] = 0.0f;
-      const int row = kb * 32 + lrow;
-#pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        const int off = ks * 64 + hgrp * 32;
-        v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (off < D) {
-          const int ch = off >> 4;
-          const v4i a = *reinterpret_cast<const v4i*>(kt + row * D + swz<KCH>(ch, k_sv(row)) * 16);
-          const v4i a2 = *reinterpret_cast<const v4i*>(kt + row * D + swz<KCH>(ch + 1, k_sv(row)) * 16);
-          kop = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
-        }
-        sacc[kb] = mfma_32x32x64_fp8(kop, qop[ks], sacc[kb]);
-      }
-    }
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mt = mx * c;
+  float alpha = 1.0f;
+  if (mt - m_run > kTau) {          // also true when m_run = -inf and mt is finite
+    alpha = fast_exp2(m_run - mt);  // 0 when m_run = -inf
+    m_run = mt;
+  }
+  const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
 
-    // ---- mask (only tiles that cross some row's key bounds) ----
-    const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
-    if (need_mask) {
+  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order; row sum of the rounded P ----
+  v8i pop[PK];
+  float lsum = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hgrp + (r & 3);
-          if (j < my_lo || j >= my_hi) sacc[kb][r] = kNegInf;
-        }
-    }
-
-    // ---- row max (lanes L and L^32 share a row), lazy rescale ----
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * c;
-    float alpha = 1.0f;
-    if (mt - m_run > kTau) {          // also true when m_run = -inf and mt is finite
-      alpha = fast_exp2(m_run - mt);  // 0 when m_run = -inf
-      m_run = mt;
-    }
-    const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
-
-    // ---- P = 2^(S*c - m + 8), row sum, E4M3 pack in PV-operand order ----
-    v8i pop;
-    float lsum = 0.0f;
+  for (int pk = 0; pk < PK; pk++)
 #pragma unroll
     for (int w = 0; w < 8; w++) {
-      const int kb = w >> 2, r0 = 4 * (w & 3);
+      const int kb = 2 * pk + (w >> 2), r0 = 4 * (w & 3);
       const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 0], c, nb));
       const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 1], c, nb));
       const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 2], c, nb));
       const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nb));
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-      pop[w] = word;
-      // the row sum is taken over the rounded P that enters the PV product, so O is an exact
-      // convex combination of V rows (weights sum to 1 whatever the E4M3 rounding)
+      pop[pk][w] = word;
       const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
       const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
       lsum += (r01[0] + r01[1]) + (r23[0] + r23[1]);
     }
-    l_run = alpha * l_run + lsum;
+  l_run = alpha * l_run + lsum;
 
-    // ---- O_tile = V^T P^T from zero, then O = alpha * O + O_tile ----
+  // ---- O_tile = V^T P^T from zero over this tile, then O = alpha * O + O_tile ----
+  const int trj = (lane & 15) >> 1;
+  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
+  const int tr_chunk_hi = (lane >> 4) & 1;
+  const int tr_byte = 8 * (lane & 1);
 #pragma unroll
-    for (int n = 0; n < NB; n++) {
+  for (int n = 0; n < NB; n++) {
+    v16f ot;
+#pragma unroll
+    for (int r = 0; r < 16; r++) ot[r] = 0.0f;
+#pragma unroll
+    for (int pk = 0; pk < PK; pk++) {
       v8i vop;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        const int row = 16 * r + tr_key;
+        const int row = 64 * pk + 16 * r + tr_key;
         const int ch = 2 * n + tr_chunk_hi;
         const int off = row * DV + swz<VCH>(ch, v_sv(row)) * 16 + tr_byte;
-        const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)((FA8_LDS uint8_t*)smem + (st * STAGE + KTILE + off)));
+        const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + off));
         vop[2 * r] = x[0];
         vop[2 * r + 1] = x[1];
       }
-      v16f zero;
-#pragma unroll
-      for (int r = 0; r < 16; r++) zero[r] = 0.0f;
-      const v16f ot = mfma_32x32x64_fp8(vop, pop, zero);
-#pragma unroll
-      for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[r]);
+      ot = mfma_32x32x64_fp8(vop, pop[pk], ot);
     }
-
-    if (t + 1 < t_end) swrite(st ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[r]);
   }
+}
 
-  // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!valid) return;
+// Final normalization and store of one lane's row (or its partial for split-KV decode).
+template <int DV, bool SPLIT>
+__device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[DV / 32], float m_run, float l_tot,
+                                          float dvs, int hgrp, int b, int q0, int qi, int qh, int split) {
+  constexpr int NB = DV / 32;
   const bool nonempty = l_tot > 0.0f;
   const float inv = nonempty ? dvs / l_tot : 0.0f;
   const float lse = nonempty ? (m_run + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
-
-  if constexpr (PACKED) {
+  if constexpr (SPLIT) {
     const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi) * p.hq + qh;
     float* orow = p.o_part + prow * DV;
 #pragma unroll
@@ -404,7 +303,8 @@ fa8_attn_kernel(const KParams p) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
         const int dvi = 32 * n + 8 * q4 + 4 * hgrp;
-        v4f v = {oacc[n][4 * q4] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv, oacc[n][4 * q4 + 3] * inv};
+        v4f v = {oacc[n][4 * q4] * inv, oacc[n][4 * q4 + 1] * inv, oacc[n][4 * q4 + 2] * inv,
+                 oacc[n][4 * q4 + 3] * inv};
         *reinterpret_cast<v4f*>(orow + dvi) = v;
       }
     if (hgrp == 0) p.lse_part[prow] = lse;
@@ -427,6 +327,308 @@ fa8_attn_kernel(const KParams p) {
       p.lse[loff] = lse;
     }
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// Full forward pass: 4 waves x 32 query rows of one query head; KV tiles of BN keys staged in
+// LDS by direct global->LDS loads (two stages, so the next tile lands while this one is used).
+// Workgroups are numbered so that each XCD (workgroup id mod 8) receives a contiguous run of
+// the work list, ordered by (batch, kv head), so the workgroups that share K/V share an L2.
+// ------------------------------------------------------------------------------------------
+template <int D, int DV, int BN>
+__global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
+  constexpr int NW = 4, BM = NW * 32;
+  constexpr int KTILE = BN * D, VTILE = BN * DV, STAGE = KTILE + VTILE;
+  constexpr int KINST = KTILE / 1024 / NW, VINST = VTILE / 1024 / NW;   // 1 KB DMA loads per wave
+  static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0, "tile must split into 1 KB loads");
+  constexpr int KCH = D / 16, VCH = DV / 16;
+  constexpr int NB = DV / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hgrp = lane >> 5, lrow = lane & 31;
+
+  // ---- XCD-aware work index ----
+  const int nwork = (int)gridDim.x;
+  const int L = (int)blockIdx.x;
+  const int xcd = L & 7, slot = L >> 3;
+  const int per = nwork >> 3, rem = nwork & 7;
+  const int w = xcd * per + min(xcd, rem) + slot;
+  const int g = p.g;
+  const int hg = w % g;
+  const int t1 = w / g;
+  const int mbi = t1 % p.nmb;
+  const int bk = t1 / p.nmb;            // b * hkv + kvh
+  const int kvh = bk % p.hkv, b = bk / p.hkv;
+  const int mblock = p.causal ? p.nmb - 1 - mbi : mbi;   // causal: heaviest row blocks first
+  const int qh = kvh * g + hg;
+
+  const SeqInfo si = seq_info(p, b);
+  const int rb0 = mblock * BM;
+  if (rb0 >= si.sq) return;  // uniform: no valid row in this block
+  const int rb1 = min(rb0 + BM, si.sq) - 1;
+  const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+  int wg_lo = rr.lo(rb0), wg_hi = rr.hi(rb1);
+  const int full_lo = rr.lo(rb1), full_hi = rr.hi(rb0);
+  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
+  const int t_begin = wg_lo / BN;
+  const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
+
+  const int qi = rb0 + wave * 32 + lrow;
+  const bool valid = qi <= rb1;
+  int my_lo = 0, my_hi = 0;
+  if (valid) {
+    my_lo = rr.lo(qi);
+    my_hi = rr.hi(qi);
+  }
+
+  const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
+  const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
+  const float dvs = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh);
+  const float c = p.scale_log2 * dq * dk;
+
+  v8i qop[(D + 63) / 64];
+  load_q<D>(p.q + (p.cu_q ? (int64_t)(si.q0 + qi) * p.q_rs : (int64_t)b * p.q_bs + (int64_t)qi * p.q_rs) +
+                (int64_t)qh * p.q_hs,
+            valid, hgrp, qop);
+
+  const KvAddr ka = kv_addr(p, b, kvh);
+  // Direct global->LDS loads of tile t into stage st. Load instruction i of this wave fills
+  // LDS bytes [1024*(wave*KINST + i), +1024) of the K tile, lane L its 16 bytes at 16*L: that
+  // position is physical chunk pc of row r, which holds logical chunk swz(pc) (an involution).
+  // Rows past the sequence read its last valid row (masked to P = 0; finite V keeps 0*V = 0).
+  auto dma_tile = [&](int t, int st) {
+    FA8_LDS uint8_t* kt = (FA8_LDS uint8_t*)smem + st * STAGE;
+    FA8_LDS uint8_t* vt = kt + KTILE;
+    const int j0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < KINST; i++) {
+      const int blk = wave * KINST + i;
+      const int pos = blk * 1024 + lane * 16;
+      const int row = pos / D, pc = (pos - row * D) >> 4;
+      const int j = min(j0 + row, si.sk - 1);
+      const uint8_t* src = p.k + ka.k(j) + swz<KCH>(pc, k_sv(row)) * 16;
+      __builtin_amdgcn_global_load_lds(src, (FA8_LDS void*)(kt + blk * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < VINST; i++) {
+      const int blk = wave * VINST + i;
+      const int pos = blk * 1024 + lane * 16;
+      const int row = pos / DV, pc = (pos - row * DV) >> 4;
+      const int j = min(j0 + row, si.sk - 1);
+      const uint8_t* src = p.v + ka.v(j) + swz<VCH>(pc, v_sv(row)) * 16;
+      __builtin_amdgcn_global_load_lds(src, (FA8_LDS void*)(vt + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.0f;
+  v16f oacc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; n++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = 0.0f;
+
+  if (t_begin < t_end) {
+    dma_tile(t_begin, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  for (int t = t_begin; t < t_end; t++) {
+    const int st = (t - t_begin) & 1;
+    if (t + 1 < t_end) dma_tile(t + 1, st ^ 1);
+    const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem + st * STAGE;
+    const int j0 = t * BN;
+    const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+    attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+    wait_vmcnt<0>();   // this wave's loads of tile t+1 have landed in LDS
+    __syncthreads();   // ... and every other wave's; all reads of stage st are done
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  store_row<DV, false>(p, oacc, m_run, l_tot, dvs, hgrp, b, si.q0, qi, qh, 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// Split-KV decode: one wave per (kv head, split, batch, row block). The q heads that share the
+// kv head are packed as rows r = i*g + (h mod g) of one 32-row block. KV tiles of 64 keys (one
+// split granule) are prefetched DEPTH tiles ahead into registers with 16-byte coalesced row
+// loads, written to a single LDS stage and consumed by attn_tile.
+// ------------------------------------------------------------------------------------------
+template <int D, int DV, int DEPTH>
+__global__ void __launch_bounds__(64) fa8_decode_kernel(const KParams p) {
+  constexpr int BN = kKvTile, BM = 32;
+  constexpr int KCH = D / 16, VCH = DV / 16;
+  constexpr int KTILE = BN * D, VTILE = BN * DV;
+  constexpr int KPT = KCH, VPT = VCH;        // 16-byte chunks per lane per tile (64 rows x NCH / 64)
+  constexpr int NB = DV / 32;
+  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[KTILE + VTILE];
+
+  const int lane = threadIdx.x;
+  const int hgrp = lane >> 5, lrow = lane & 31;
+  const int b = blockIdx.z;
+  const int split = blockIdx.y;
+  const int kvh = blockIdx.x / p.nmb;
+  const int mblock = blockIdx.x - kvh * p.nmb;
+  const int g = p.g;
+
+  const SeqInfo si = seq_info(p, b);
+  const int rows_total = si.sq * g;
+  const int rb0 = mblock * BM;
+  if (rb0 >= rows_total) return;
+  const int rb1 = min(rb0 + BM, rows_total) - 1;
+  const int i_first = rb0 / g, i_last = rb1 / g;
+  const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+  int wg_lo = rr.lo(i_first), wg_hi = rr.hi(i_last);
+  int full_lo = rr.lo(i_last), full_hi = rr.hi(i_first);
+  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
+  {
+    // split s covers granules [g0 + s*n/S, g0 + (s+1)*n/S) of the block's granule range
+    const int g0 = wg_lo / BN, g1 = (wg_hi + BN - 1) / BN, n = g1 - g0;
+    const int s0 = g0 + (int)(((int64_t)split * n) / p.nsplit);
+    const int s1 = g0 + (int)(((int64_t)(split + 1) * n) / p.nsplit);
+    wg_lo = max(wg_lo, s0 * BN);
+    wg_hi = min(wg_hi, s1 * BN);
+    full_lo = max(full_lo, s0 * BN);
+    full_hi = min(full_hi, s1 * BN);
+  }
+  const int t_begin = wg_lo / BN;
+  const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
+
+  const int ridx = rb0 + lrow;
+  const bool valid = ridx <= rb1;
+  const int qi = ridx / g;
+  const int qh = kvh * g + (ridx - qi * g);
+  int my_lo = 0, my_hi = 0;
+  if (valid) {
+    my_lo = max(rr.lo(qi), wg_lo);
+    my_hi = min(rr.hi(qi), wg_hi);
+  }
+
+  const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
+  const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
+  const float dvs = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh);
+  const float c = p.scale_log2 * dq * dk;
+
+  v8i qop[(D + 63) / 64];
+  load_q<D>(p.q + (p.cu_q ? (int64_t)(si.q0 + qi) * p.q_rs : (int64_t)b * p.q_bs + (int64_t)qi * p.q_rs) +
+                (int64_t)qh * p.q_hs,
+            valid, hgrp, qop);
+
+  const KvAddr ka = kv_addr(p, b, kvh);
+  // When the rows of one load instruction (64 lanes x 16 bytes = 64/NCH rows) always lie in one
+  // page, that page's table entry is wave-uniform and is read with a scalar load, which does
+  // not wait behind the vector loads still in flight (their counter completes in order).
+  const bool k_uniform_page = ka.trow && (64 % KCH == 0) && (p.page_shift >= 0) && ((1 << p.page_shift) >= 64 / KCH);
+  const bool v_uniform_page = ka.trow && (64 % VCH == 0) && (p.page_shift >= 0) && ((1 << p.page_shift) >= 64 / VCH);
+  // chunk u of this lane: linear chunk id u*64 + lane of the tile -> (row, 16-byte chunk)
+  auto gload = [&](int t, v4i (&kr)[KPT], v4i (&vr)[VPT]) {
+    const int j0 = t * BN;
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+      const int cid = u * 64 + lane;
+      const int row = cid / KCH, ch = cid - row * KCH;
+      const int j = j0 + row;
+      v4i x = {0, 0, 0, 0};
+      if (k_uniform_page) {
+        const int jr = j0 + (u * 64) / KCH;          // first row of this instruction, uniform
+        if (jr < si.sk) {
+          const int64_t base = (int64_t)ka.trow[jr >> ka.shift] * ka.k_ps + ka.kbase;
+          if (j < si.sk) x = ld_global16(p.k + base + (int64_t)(j & ka.pmask) * ka.k_rs + ch * 16);
+        }
+      } else if (j < si.sk) {
+        x = ld_global16(p.k + ka.k(j) + ch * 16);
+      }
+      kr[u] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+      const int cid = u * 64 + lane;
+      const int row = cid / VCH, ch = cid - row * VCH;
+      const int j = j0 + row;
+      v4i x = {0, 0, 0, 0};
+      if (v_uniform_page) {
+        const int jr = j0 + (u * 64) / VCH;
+        if (jr < si.sk) {
+          const int64_t base = (int64_t)ka.trow[jr >> ka.shift] * ka.v_ps + ka.vbase;
+          if (j < si.sk) x = ld_global16(p.v + base + (int64_t)(j & ka.pmask) * ka.v_rs + ch * 16);
+        }
+      } else if (j < si.sk) {
+        x = ld_global16(p.v + ka.v(j) + ch * 16);
+      }
+      vr[u] = x;
+    }
+  };
+  auto swrite = [&](const v4i (&kr)[KPT], const v4i (&vr)[VPT]) {
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+      const int cid = u * 64 + lane;
+      const int row = cid / KCH, ch = cid - row * KCH;
+      *reinterpret_cast<v4i*>(smem + row * D + swz<KCH>(ch, k_sv(row)) * 16) = kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+      const int cid = u * 64 + lane;
+      const int row = cid / VCH, ch = cid - row * VCH;
+      *reinterpret_cast<v4i*>(smem + KTILE + row * DV + swz<VCH>(ch, v_sv(row)) * 16) = vr[u];
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.0f;
+  v16f oacc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; n++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = 0.0f;
+
+  const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem;
+  auto consume = [&](int t, const v4i (&kr)[KPT], const v4i (&vr)[VPT]) {
+    __syncthreads();   // every lane's reads of the previous tile are done
+    swrite(kr, vr);
+    __syncthreads();   // the tile is in LDS for every lane
+    const int j0 = t * BN;
+    const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+    attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+  };
+
+  v4i kr0[KPT], vr0[VPT];
+  if constexpr (DEPTH == 2) {
+    v4i kr1[KPT], vr1[VPT];
+    if (t_begin < t_end) gload(t_begin, kr0, vr0);
+    if (t_begin + 1 < t_end) gload(t_begin + 1, kr1, vr1);
+    for (int t = t_begin; t < t_end; t += 2) {
+      // tile t is in kr0/vr0, tile t+1 (if any) in flight into kr1/vr1
+      __syncthreads();
+      swrite(kr0, vr0);
+      __syncthreads();
+      if (t + 2 < t_end) gload(t + 2, kr0, vr0);
+      {
+        const int j0 = t * BN;
+        const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+        attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+      }
+      if (t + 1 < t_end) {
+        __syncthreads();
+        swrite(kr1, vr1);
+        __syncthreads();
+        if (t + 3 < t_end) gload(t + 3, kr1, vr1);
+        const int j0 = (t + 1) * BN;
+        const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+        attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+      }
+    }
+  } else {
+    for (int t = t_begin; t < t_end; t++) {
+      gload(t, kr0, vr0);
+      consume(t, kr0, vr0);
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!valid) return;
+  store_row<DV, true>(p, oacc, m_run, l_tot, dvs, hgrp, b, si.q0, qi, qh, split);
 }
 
 // Log-sum-exp merge of split partials: one thread per 4 output elements of one row.
@@ -469,18 +671,23 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   }
 }
 
+// KV tile of the prefill kernel: 128 keys when a two-stage tile pair fits twice in LDS, else 64.
+template <int D, int DV>
+constexpr int prefill_tile() { return (D + DV) <= 256 ? 128 : 64; }
+template <int D, int DV>
+constexpr int decode_depth() { return (D + DV) <= 320 ? 2 : 1; }
+
 template <int D, int DV>
 static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
-  constexpr int NW = kPrefillRows / 32;
-  dim3 grid((unsigned)kp.nmb, (unsigned)kp.hq, (unsigned)kp.batch);
-  hipLaunchKernelGGL((fa8_attn_kernel<D, DV, NW, false>), grid, dim3(NW * 64), 0, stream, kp);
+  const int64_t nwork = (int64_t)kp.nmb * kp.hq * kp.batch;
+  hipLaunchKernelGGL((fa8_prefill_kernel<D, DV, prefill_tile<D, DV>()>), dim3((unsigned)nwork), dim3(256), 0,
+                     stream, kp);
   return hipGetLastError();
 }
 template <int D, int DV>
 static hipError_t launch_decode_t(const KParams& kp, hipStream_t stream) {
-  constexpr int NW = kDecodeRows / 32;
   dim3 grid((unsigned)(kp.hkv * kp.nmb), (unsigned)kp.nsplit, (unsigned)kp.batch);
-  hipLaunchKernelGGL((fa8_attn_kernel<D, DV, NW, true>), grid, dim3(NW * 64), 0, stream, kp);
+  hipLaunchKernelGGL((fa8_decode_kernel<D, DV, decode_depth<D, DV>()>), grid, dim3(64), 0, stream, kp);
   return hipGetLastError();
 }
 

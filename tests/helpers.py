@@ -134,12 +134,18 @@ def split_key_ranges(inp, num_splits: int):
     return (rb, rh, ri), ranges
 
 
-def emulate_full(inp, num_splits: int = 1, with_lse: bool = False, **kw):
+def prefill_tile(d: int, dv: int) -> int:
+    """KV tile of the prefill kernel: 128 keys when d + dv <= 256, else 64 (the lazy-rescale
+    decisions, and so the exact rounding, depend on the tile the kernel uses)."""
+    return 128 if d + dv <= 256 else 64
+
+
+def emulate_full(inp, num_splits: int = 1, with_lse: bool = False, tile_n: int = GRANULE, **kw):
     """The oracle package's step-by-step method emulator, reshaped to the output layout (and the
     LSE to [B, Hq, Sq] / [Hq, total_q] when with_lse)."""
     from oracle import emulator
     kw.setdefault("l_from_rounded", True)      # the kernel sums the rounded P
-    res = emulator.emulate(inp, tile_n=GRANULE, num_splits=num_splits, **kw)
+    res = emulator.emulate(inp, tile_n=tile_n, num_splits=num_splits, **kw)
     if inp.cu_seqlens_q is not None:
         tot = int(inp.cu_seqlens_q[-1])
         out = np.zeros((tot, inp.heads_q, inp.dv))
@@ -205,7 +211,7 @@ def compare_to_emulator(got, emu, ref, what=""):
 LSE_METHOD = -math.log(1 - 2.0 ** -4) + 1e-4
 
 
-def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits=1):
+def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits=1, tile_n=GRANULE):
     """Parity of one kernel result with the oracle.
 
     strict: every element within 2e-2 + 2e-2 |ref| (the stated tolerance), except elements where
@@ -224,7 +230,7 @@ def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits
     bound = method_bound(inp, ref)
     emu_o = emu_l = None
     if emu:
-        emu_o, emu_l = emulate_full(inp, num_splits=num_splits, with_lse=True)
+        emu_o, emu_l = emulate_full(inp, num_splits=num_splits, with_lse=True, tile_n=tile_n)
     n_method = 0
     if strict:
         bad = err > ATOL + RTOL * np.abs(ref)

@@ -10,19 +10,19 @@ import oracle
 from fa8_fwd_amd import binding
 from fa8_fwd_amd import inputs as gen
 
-from helpers import (check_against_oracle, compare, compare_lse, run_decode, run_prefill, split_key_ranges,
-                     tensors)
+from helpers import (GRANULE, check_against_oracle, compare, compare_lse, prefill_tile, run_decode, run_prefill,
+                     split_key_ranges, tensors)
 
 pytestmark = pytest.mark.gpu
 
 
-def _check(inp, got, glse, what, strict=True, emu=True, num_splits=1):
-    print(check_against_oracle(inp, got, glse, what, strict, emu, num_splits), flush=True)
+def _check(inp, got, glse, what, strict=True, emu=True, num_splits=1, tile_n=GRANULE):
+    print(check_against_oracle(inp, got, glse, what, strict, emu, num_splits, tile_n), flush=True)
 
 
 def _prefill_check(inp, what, strict=True, emu=True):
     got, glse = run_prefill(inp)
-    _check(inp, got, glse, what, strict, emu)
+    _check(inp, got, glse, what, strict, emu, tile_n=prefill_tile(inp.d, inp.dv))
     return got
 
 
@@ -78,7 +78,7 @@ def test_prefill_varlen_empty_rows():
 def test_prefill_paged_equals_contiguous_bitwise():
     inp = gen.make_paged(7, [300, 17, 640, 129], 8, 2, 128, 128, page_size=16, sq=40, varlen_q=False, causal=True)
     got, glse = run_prefill(inp)
-    _check(inp, got, glse, "paged prefill", strict=False)   # a 17-key sequence
+    _check(inp, got, glse, "paged prefill", strict=False, tile_n=prefill_tile(128, 128))   # a 17-key sequence
     # same tokens, contiguous varlen K/V
     sk = inp.seqused_k.astype(np.int64)
     ks, vs = [], []
@@ -116,7 +116,7 @@ def test_descale_modes(mode):
         dq = rng.uniform(0.5, 2, (1, 2)).astype(np.float32)
         inp.q_descale = dq
     got, glse = run_prefill(inp)
-    _check(inp, got, glse, f"descales {mode}", strict=False)
+    _check(inp, got, glse, f"descales {mode}", strict=False, tile_n=prefill_tile(128, 128))
 
 
 def _decode_check(inp, num_splits, what, strict=True, emu=True):
