@@ -53,6 +53,10 @@ __device__ __forceinline__ v16f mfma_32x32x64_fp8(v8i a, v8i b, v16f c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ v4f mfma_16x16x128_fp8(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // s_waitcnt with only the vector-memory counter limited (gfx9 encoding: vmcnt in bits 3:0 and
@@ -62,6 +66,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// Orders this wave's LDS accesses in the compiler's view without a hardware barrier: a wave's
+// LDS instructions execute in issue order, so a one-wave workgroup exchanging data between its
+// lanes through LDS only needs the compiler to keep program order. (__syncthreads would also
+// wait for every outstanding global load, draining the prefetched tiles.)
+__device__ __forceinline__ void wave_lds_order() { __asm__ __volatile__("" ::: "memory"); }
 
 // Position of 16-byte chunk `ch` of a row holding NCH chunks, XOR-swizzled by `sv` inside the
 // largest aligned power-of-two group of chunks that fits in the row (an involution).
@@ -76,6 +86,8 @@ __device__ __forceinline__ int k_sv(int row) { return row & 7; }
 // V is read 8 rows at a time by ds_read_b64_tr_b8 with row sets {0-3, 8-11} + 4h (+16r):
 // bits 0, 1 and 3 of the row make those 8 rows land in 8 different chunks.
 __device__ __forceinline__ int v_sv(int row) { return (row & 3) | ((row >> 1) & 4); }
+// Same for the 16x16 decode tile, whose transposed V reads touch rows {0-3, 16-19} + 4h (+32r).
+__device__ __forceinline__ int v_sv16(int row) { return (row & 3) | ((row >> 2) & 4); }
 
 __device__ __forceinline__ v4i ld_global16(const uint8_t* ptr) {
   return *reinterpret_cast<const v4i*>(ptr);
@@ -287,6 +299,112 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
 }
 
+// One 64-key tile for decode, on the 16x16x128 FP8 MFMA: NQB blocks of 16 query rows (decode
+// rows are few, so 16-wide blocks waste less than 32-wide ones). Lane L owns query row L%16 of
+// each block and the keys 16kb + 4*(L/16) + r of the S^T accumulators; the PV product runs over
+// a 128-key contraction whose upper 64 keys are zero (the tile has 64). Row max and row sum
+// combine the four lanes L, L^16, L^32, L^48 of a row.
+template <int D, int DV, int NQB>
+__device__ __forceinline__ void attn_tile16(const FA8_LDS uint8_t* kt, const FA8_LDS uint8_t* vt,
+                                            const v8i (&qop)[NQB][(D + 127) / 128], float c, bool need_mask,
+                                            int j0, const int (&my_lo)[NQB], const int (&my_hi)[NQB], int lane,
+                                            float (&m_run)[NQB], float (&l_run)[NQB],
+                                            v4f (&oacc)[NQB][DV / 16]) {
+  constexpr int KS = (D + 127) / 128;
+  constexpr int NB = DV / 16;
+  constexpr int KCH = D / 16, VCH = DV / 16;
+  const int h = lane >> 4, l16 = lane & 15;
+
+  // ---- S^T = K Q^T: 4 blocks of 16 keys ----
+  v4f sacc[NQB][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; qb++) sacc[qb][kb] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    const int row = kb * 16 + l16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int off = ks * 128 + h * 32;
+      v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (off < D) {
+        const int ch = off >> 4;
+        const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch, k_sv(row)) * 16);
+        const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch + 1, k_sv(row)) * 16);
+        kop = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+      }
+#pragma unroll
+      for (int qb = 0; qb < NQB; qb++) sacc[qb][kb] = mfma_16x16x128_fp8(kop, qop[qb][ks], sacc[qb][kb]);
+    }
+  }
+
+  v8i pop[NQB];
+  float alpha[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; qb++) {
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int j = j0 + kb * 16 + 4 * h + r;
+          if (j < my_lo[qb] || j >= my_hi[qb]) sacc[qb][kb][r] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) mx = fmaxf(mx, fmaxf(fmaxf(sacc[qb][kb][0], sacc[qb][kb][1]),
+                                                     fmaxf(sacc[qb][kb][2], sacc[qb][kb][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * c;
+    alpha[qb] = 1.0f;
+    if (mt - m_run[qb] > kTau) {
+      alpha[qb] = fast_exp2(m_run[qb] - mt);
+      m_run[qb] = mt;
+    }
+    const float nb = (m_run[qb] == kNegInf) ? 0.0f : kBias - m_run[qb];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float p0 = fast_exp2(__builtin_fmaf(sacc[qb][w][0], c, nb));
+      const float p1 = fast_exp2(__builtin_fmaf(sacc[qb][w][1], c, nb));
+      const float p2 = fast_exp2(__builtin_fmaf(sacc[qb][w][2], c, nb));
+      const float p3 = fast_exp2(__builtin_fmaf(sacc[qb][w][3], c, nb));
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+      pop[qb][w] = word;
+      pop[qb][w + 4] = 0;
+      const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      lsum += (r01[0] + r01[1]) + (r23[0] + r23[1]);
+    }
+    l_run[qb] = alpha[qb] * l_run[qb] + lsum;
+  }
+
+  // ---- O_tile = V^T P^T from zero, then O = alpha * O + O_tile ----
+  const int trj = l16 >> 1;
+  const int tr_key = 16 * (trj >> 2) + 4 * h + (trj & 3);
+  const int tr_byte = 8 * (lane & 1);
+#pragma unroll
+  for (int n = 0; n < NB; n++) {
+    v8i vop = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      const int row = 32 * r + tr_key;
+      const int off = row * DV + swz<VCH>(n, v_sv16(row)) * 16 + tr_byte;
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + off));
+      vop[2 * r] = x[0];
+      vop[2 * r + 1] = x[1];
+    }
+#pragma unroll
+    for (int qb = 0; qb < NQB; qb++) {
+      const v4f ot = mfma_16x16x128_fp8(vop, pop[qb], (v4f){0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+      for (int r = 0; r < 4; r++) oacc[qb][n][r] = __builtin_fmaf(alpha[qb], oacc[qb][n][r], ot[r]);
+    }
+  }
+}
+
 // Final normalization and store of one lane's row (or its partial for split-KV decode).
 template <int DV, bool SPLIT>
 __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[DV / 32], float m_run, float l_tot,
@@ -452,22 +570,37 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
 
 // ------------------------------------------------------------------------------------------
 // Split-KV decode: one wave per (kv head, split, batch, row block). The q heads that share the
-// kv head are packed as rows r = i*g + (h mod g) of one 32-row block. KV tiles of 64 keys (one
-// split granule) are prefetched DEPTH tiles ahead into registers with 16-byte coalesced row
-// loads, written to a single LDS stage and consumed by attn_tile.
+// kv head are packed as rows r = i*g + (h mod g) of one block of up to 32 rows, handled as NQB
+// blocks of 16 by the 16x16x128 MFMA. KV tiles of 64 keys (one split granule) go global ->
+// registers -> one LDS stage; the next tile's loads are issued as soon as the current tile is
+// in LDS, so they are in flight while it is computed (about 16 KB per wave, with two waves per
+// SIMD).
+//
+// Paged K/V (PAGEMODE 1 and 2) walks the split in windows of 64 block-table entries: one vector
+// load puts page win_base + i in lane i, then every tile inside the window takes its page
+// numbers from that register, by v_readlane when each load instruction's rows lie in one page
+// (PAGEMODE 1: page_size >= 64 / (d/16)) or by a lane shuffle (PAGEMODE 2). The tile loop has
+// no branches around its loads, so the compiler's in-order vector-memory wait counts stay
+// exact. Contiguous K/V is PAGEMODE 0.
 // ------------------------------------------------------------------------------------------
-template <int D, int DV, int DEPTH>
-__global__ void __launch_bounds__(64) fa8_decode_kernel(const KParams p) {
-  constexpr int BN = kKvTile, BM = 32;
+// Waves per SIMD the decode kernel is compiled for: two when its registers fit in 256.
+template <int D, int DV, int NQB>
+constexpr int decode_waves() { return (NQB == 1 && D + DV <= 256) ? 2 : 1; }
+
+template <int D, int DV, int NQB, int PAGEMODE>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_waves<D, DV, NQB>(), 8)))
+fa8_decode_kernel(const KParams p) {
+  constexpr int BN = kKvTile;
   constexpr int KCH = D / 16, VCH = DV / 16;
   constexpr int KTILE = BN * D, VTILE = BN * DV;
   constexpr int KPT = KCH, VPT = VCH;        // 16-byte chunks per lane per tile (64 rows x NCH / 64)
-  constexpr int NB = DV / 32;
-  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth");
+  constexpr int KS = (D + 127) / 128;
+  constexpr int NB = DV / 16;
+  constexpr int BM = 32;                     // rows of a decode block (NQB * 16 of them are computed)
   __shared__ __attribute__((aligned(16))) uint8_t smem[KTILE + VTILE];
 
   const int lane = threadIdx.x;
-  const int hgrp = lane >> 5, lrow = lane & 31;
+  const int h4 = lane >> 4, l16 = lane & 15;
   const int b = blockIdx.z;
   const int split = blockIdx.y;
   const int kvh = blockIdx.x / p.nmb;
@@ -497,71 +630,82 @@ __global__ void __launch_bounds__(64) fa8_decode_kernel(const KParams p) {
   const int t_begin = wg_lo / BN;
   const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
 
-  const int ridx = rb0 + lrow;
-  const bool valid = ridx <= rb1;
-  const int qi = ridx / g;
-  const int qh = kvh * g + (ridx - qi * g);
-  int my_lo = 0, my_hi = 0;
-  if (valid) {
-    my_lo = max(rr.lo(qi), wg_lo);
-    my_hi = min(rr.hi(qi), wg_hi);
-  }
-
   const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
   const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
   const float dvs = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh);
   const float c = p.scale_log2 * dq * dk;
 
-  v8i qop[(D + 63) / 64];
-  load_q<D>(p.q + (p.cu_q ? (int64_t)(si.q0 + qi) * p.q_rs : (int64_t)b * p.q_bs + (int64_t)qi * p.q_rs) +
-                (int64_t)qh * p.q_hs,
-            valid, hgrp, qop);
+  // this lane's row in each 16-row block: Q as the B operand, d-bytes [128ks + 32*h4, +32)
+  bool valid[NQB];
+  int qi[NQB], qh[NQB], my_lo[NQB], my_hi[NQB];
+  v8i qop[NQB][KS];
+#pragma unroll
+  for (int qb = 0; qb < NQB; qb++) {
+    const int ridx = rb0 + qb * 16 + l16;
+    valid[qb] = ridx <= rb1;
+    qi[qb] = ridx / g;
+    qh[qb] = kvh * g + (ridx - qi[qb] * g);
+    my_lo[qb] = 0;
+    my_hi[qb] = 0;
+    if (valid[qb]) {
+      my_lo[qb] = max(rr.lo(qi[qb]), wg_lo);
+      my_hi[qb] = min(rr.hi(qi[qb]), wg_hi);
+    }
+    const uint8_t* qrow = p.q + (p.cu_q ? (int64_t)(si.q0 + qi[qb]) * p.q_rs
+                                        : (int64_t)b * p.q_bs + (int64_t)qi[qb] * p.q_rs) +
+                          (int64_t)qh[qb] * p.q_hs;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int off = ks * 128 + h4 * 32;
+      v4i x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+      if (valid[qb] && off < D) {
+        x0 = ld_global16(qrow + off);
+        x1 = ld_global16(qrow + off + 16);
+      }
+      qop[qb][ks] = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+  }
 
   const KvAddr ka = kv_addr(p, b, kvh);
-  // When the rows of one load instruction (64 lanes x 16 bytes = 64/NCH rows) always lie in one
-  // page, that page's table entry is wave-uniform and is read with a scalar load, which does
-  // not wait behind the vector loads still in flight (their counter completes in order).
-  const bool k_uniform_page = ka.trow && (64 % KCH == 0) && (p.page_shift >= 0) && ((1 << p.page_shift) >= 64 / KCH);
-  const bool v_uniform_page = ka.trow && (64 % VCH == 0) && (p.page_shift >= 0) && ((1 << p.page_shift) >= 64 / VCH);
-  // chunk u of this lane: linear chunk id u*64 + lane of the tile -> (row, 16-byte chunk)
-  auto gload = [&](int t, v4i (&kr)[KPT], v4i (&vr)[VPT]) {
+  const int jlast = si.sk - 1;
+  int win_base = 0, win_val = 0;
+
+  // 16-byte chunk (row, ch) of tile j0, load instruction with first row j0 + r0. The row is
+  // clamped to the last valid one: rows past the sequence are masked to P = 0 and the clamped V
+  // row is finite, so they contribute exactly 0.
+  auto chunk_ptr = [&](const uint8_t* base_ptr, int64_t kvbase, int64_t pstride, int64_t rstride, int j0, int r0,
+                       int row, int ch) -> const uint8_t* {
+    const int j = min(j0 + row, jlast);
+    if constexpr (PAGEMODE == 0) {
+      const uint8_t* base = base_ptr + kvbase + (int64_t)j0 * rstride;          // uniform
+      return base + (uint32_t)((j - j0) * (int)rstride + ch * 16);
+    } else if constexpr (PAGEMODE == 1) {
+      const int jr = min(j0 + r0, jlast);
+      const int page = __builtin_amdgcn_readlane(win_val, (jr >> ka.shift) - win_base);
+      const uint8_t* base = base_ptr + kvbase + (int64_t)page * pstride;       // uniform
+      return base + (uint32_t)((j & ka.pmask) * (int)rstride + ch * 16);
+    } else {
+      const int page = __shfl(win_val, (j >> ka.shift) - win_base);
+      return base_ptr + kvbase + (int64_t)page * pstride + (int64_t)(j & ka.pmask) * rstride + ch * 16;
+    }
+  };
+  v4i kr[KPT], vr[VPT];
+  auto gload = [&](int t) {
     const int j0 = t * BN;
 #pragma unroll
     for (int u = 0; u < KPT; u++) {
       const int cid = u * 64 + lane;
       const int row = cid / KCH, ch = cid - row * KCH;
-      const int j = j0 + row;
-      v4i x = {0, 0, 0, 0};
-      if (k_uniform_page) {
-        const int jr = j0 + (u * 64) / KCH;          // first row of this instruction, uniform
-        if (jr < si.sk) {
-          const int64_t base = (int64_t)ka.trow[jr >> ka.shift] * ka.k_ps + ka.kbase;
-          if (j < si.sk) x = ld_global16(p.k + base + (int64_t)(j & ka.pmask) * ka.k_rs + ch * 16);
-        }
-      } else if (j < si.sk) {
-        x = ld_global16(p.k + ka.k(j) + ch * 16);
-      }
-      kr[u] = x;
+      kr[u] = ld_global16(chunk_ptr(p.k, ka.kbase, ka.k_ps, ka.k_rs, j0, (u * 64) / KCH, row, ch));
     }
 #pragma unroll
     for (int u = 0; u < VPT; u++) {
       const int cid = u * 64 + lane;
       const int row = cid / VCH, ch = cid - row * VCH;
-      const int j = j0 + row;
-      v4i x = {0, 0, 0, 0};
-      if (v_uniform_page) {
-        const int jr = j0 + (u * 64) / VCH;
-        if (jr < si.sk) {
-          const int64_t base = (int64_t)ka.trow[jr >> ka.shift] * ka.v_ps + ka.vbase;
-          if (j < si.sk) x = ld_global16(p.v + base + (int64_t)(j & ka.pmask) * ka.v_rs + ch * 16);
-        }
-      } else if (j < si.sk) {
-        x = ld_global16(p.v + ka.v(j) + ch * 16);
-      }
-      vr[u] = x;
+      vr[u] = ld_global16(chunk_ptr(p.v, ka.vbase, ka.v_ps, ka.v_rs, j0, (u * 64) / VCH, row, ch));
     }
   };
-  auto swrite = [&](const v4i (&kr)[KPT], const v4i (&vr)[VPT]) {
+  auto swrite = [&]() {
 #pragma unroll
     for (int u = 0; u < KPT; u++) {
       const int cid = u * 64 + lane;
@@ -572,63 +716,71 @@ __global__ void __launch_bounds__(64) fa8_decode_kernel(const KParams p) {
     for (int u = 0; u < VPT; u++) {
       const int cid = u * 64 + lane;
       const int row = cid / VCH, ch = cid - row * VCH;
-      *reinterpret_cast<v4i*>(smem + KTILE + row * DV + swz<VCH>(ch, v_sv(row)) * 16) = vr[u];
+      *reinterpret_cast<v4i*>(smem + KTILE + row * DV + swz<VCH>(ch, v_sv16(row)) * 16) = vr[u];
     }
   };
 
-  float m_run = kNegInf, l_run = 0.0f;
-  v16f oacc[NB];
+  float m_run[NQB], l_run[NQB];
+  v4f oacc[NQB][NB];
 #pragma unroll
-  for (int n = 0; n < NB; n++)
+  for (int qb = 0; qb < NQB; qb++) {
+    m_run[qb] = kNegInf;
+    l_run[qb] = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = 0.0f;
+    for (int n = 0; n < NB; n++) oacc[qb][n] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
   const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem;
-  auto consume = [&](int t, const v4i (&kr)[KPT], const v4i (&vr)[VPT]) {
-    __syncthreads();   // every lane's reads of the previous tile are done
-    swrite(kr, vr);
-    __syncthreads();   // the tile is in LDS for every lane
-    const int j0 = t * BN;
-    const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
-    attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+  // Tiles [w0, w1): tile t goes registers -> LDS, then tile t+1's loads are issued (a scheduling
+  // barrier keeps them ahead of the compute), then tile t is computed from LDS.
+  auto run_tiles = [&](int w0, int w1) {
+    gload(w0);
+    for (int t = w0; t < w1; t++) {
+      wave_lds_order();   // the previous tile's LDS reads are issued before these writes
+      swrite();
+      wave_lds_order();
+      if (t + 1 < w1) gload(t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int j0 = t * BN;
+      const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+      attn_tile16<D, DV, NQB>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+    }
   };
 
-  v4i kr0[KPT], vr0[VPT];
-  if constexpr (DEPTH == 2) {
-    v4i kr1[KPT], vr1[VPT];
-    if (t_begin < t_end) gload(t_begin, kr0, vr0);
-    if (t_begin + 1 < t_end) gload(t_begin + 1, kr1, vr1);
-    for (int t = t_begin; t < t_end; t += 2) {
-      // tile t is in kr0/vr0, tile t+1 (if any) in flight into kr1/vr1
-      __syncthreads();
-      swrite(kr0, vr0);
-      __syncthreads();
-      if (t + 2 < t_end) gload(t + 2, kr0, vr0);
-      {
-        const int j0 = t * BN;
-        const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
-        attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
-      }
-      if (t + 1 < t_end) {
-        __syncthreads();
-        swrite(kr1, vr1);
-        __syncthreads();
-        if (t + 3 < t_end) gload(t + 3, kr1, vr1);
-        const int j0 = (t + 1) * BN;
-        const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
-        attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
-      }
-    }
+  if constexpr (PAGEMODE == 0) {
+    if (t_begin < t_end) run_tiles(t_begin, t_end);
   } else {
-    for (int t = t_begin; t < t_end; t++) {
-      gload(t, kr0, vr0);
-      consume(t, kr0, vr0);
+    const int last_page = jlast >> ka.shift;
+    int t = t_begin;
+    while (t < t_end) {
+      // window of 64 entries from this tile's first page; then the tiles whose rows all fall in it
+      win_base = (t * BN) >> ka.shift;
+      win_val = ka.trow[min(win_base + lane, last_page)];
+      wait_vmcnt<0>();
+      int w1 = t + 1;
+      while (w1 < t_end && ((min(w1 * BN + BN - 1, jlast) >> ka.shift) - win_base) < 64) w1++;
+      run_tiles(t, w1);
+      t = w1;
     }
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!valid) return;
-  store_row<DV, true>(p, oacc, m_run, l_tot, dvs, hgrp, b, si.q0, qi, qh, split);
+#pragma unroll
+  for (int qb = 0; qb < NQB; qb++) {
+    float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!valid[qb]) continue;
+    const bool nonempty = l_tot > 0.0f;
+    const float inv = nonempty ? dvs / l_tot : 0.0f;
+    const float lse = nonempty ? (m_run[qb] + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
+    const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi[qb]) * p.hq + qh[qb];
+    float* orow = p.o_part + prow * DV;
+#pragma unroll
+    for (int n = 0; n < NB; n++) {
+      v4f v = {oacc[qb][n][0] * inv, oacc[qb][n][1] * inv, oacc[qb][n][2] * inv, oacc[qb][n][3] * inv};
+      *reinterpret_cast<v4f*>(orow + 16 * n + 4 * h4) = v;
+    }
+    if (h4 == 0) p.lse_part[prow] = lse;
+  }
 }
 
 // Log-sum-exp merge of split partials: one thread per 4 output elements of one row.
@@ -674,8 +826,6 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
 // KV tile of the prefill kernel: 128 keys when a two-stage tile pair fits twice in LDS, else 64.
 template <int D, int DV>
 constexpr int prefill_tile() { return (D + DV) <= 256 ? 128 : 64; }
-template <int D, int DV>
-constexpr int decode_depth() { return (D + DV) <= 320 ? 2 : 1; }
 
 template <int D, int DV>
 static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
@@ -684,10 +834,26 @@ static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
                      stream, kp);
   return hipGetLastError();
 }
+template <int D, int DV, int NQB>
+static void launch_decode_q(const KParams& kp, dim3 grid, hipStream_t stream) {
+  // the rows of one 64-lane load instruction (64 / (d/16) rows) lie in one page
+  constexpr int rows_k = (64 % (D / 16) == 0) ? 64 / (D / 16) : 1 << 30;
+  constexpr int rows_v = (64 % (DV / 16) == 0) ? 64 / (DV / 16) : 1 << 30;
+  if (kp.page_shift < 0)
+    hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 0>), grid, dim3(64), 0, stream, kp);
+  else if ((1 << kp.page_shift) >= rows_k && (1 << kp.page_shift) >= rows_v)
+    hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 1>), grid, dim3(64), 0, stream, kp);
+  else
+    hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 2>), grid, dim3(64), 0, stream, kp);
+}
 template <int D, int DV>
 static hipError_t launch_decode_t(const KParams& kp, hipStream_t stream) {
   dim3 grid((unsigned)(kp.hkv * kp.nmb), (unsigned)kp.nsplit, (unsigned)kp.batch);
-  hipLaunchKernelGGL((fa8_decode_kernel<D, DV, decode_depth<D, DV>()>), grid, dim3(64), 0, stream, kp);
+  // blocks hold min(32, Sq * g) rows: one 16-row MFMA block suffices up to 16
+  if ((int64_t)kp.max_sq * kp.g <= 16)
+    launch_decode_q<D, DV, 1>(kp, grid, stream);
+  else
+    launch_decode_q<D, DV, 2>(kp, grid, stream);
   return hipGetLastError();
 }
 
