@@ -264,7 +264,7 @@ def main():
                    "d": dec.d, "page_size": dec.page_size, "seqlens_k": "uniform [1024, 8192], seed 1",
                    "sum_seqlen_k": int(dec.seqlens_k().sum()), "num_splits": S, "out": "bf16",
                    "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": "fa8_attn_kernel<128,128,1,true> (split-KV decode)",
+        "roofline": {"bound": "hbm", "kernel": "fa8_decode_kernel<128,128,1,1> (split-KV decode, paged)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel_ms": round(kern_ms, 5), "bytes_per_launch": kbytes},
@@ -278,7 +278,7 @@ def main():
         line["prefill"] = {
             "workload": pre.name, "value": round(tfl, 2), "unit": "TFLOP/s", "ms_per_step": round(p_ms, 4),
             "steps": args.prefill_steps, "flop_per_step": flop, "pct_of_fp8_peak": round(100 * tfl / FP8_PEAK_TFLOPS, 2),
-            "roofline": {"bound": "mfma", "kernel": "fa8_attn_kernel<128,128,4,false> (prefill)",
+            "roofline": {"bound": "mfma", "kernel": "fa8_prefill_kernel<128,128,128> (prefill)",
                          "achieved": round(ktfl, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ktfl / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel_ms": round(p_kern, 4)},
         }

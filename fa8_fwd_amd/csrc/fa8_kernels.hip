@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa8_internal.h"
 
 namespace fa8 {
@@ -47,6 +49,10 @@ constexpr float kTau = 0.75f;    // lazy-rescale slack in log2 units, <= log2(44
 constexpr float kBias = 8.0f;    // P is computed as 2^(x - m + 8)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// 1 KB read by the decode kernel's pipeline-filler loads (one 16-byte chunk per lane): a small
+// block that stays cached, so those loads cost no HBM traffic. Never written.
+__device__ __attribute__((aligned(1024))) uint8_t g_filler[1024];
 
 __device__ __forceinline__ v16f mfma_32x32x64_fp8(v8i a, v8i b, v16f c) {
   // format codes 0/0 = E4M3 for both operands; zero scale operands select the unscaled MFMA
@@ -91,6 +97,22 @@ __device__ __forceinline__ int v_sv16(int row) { return (row & 3) | ((row >> 2) 
 
 __device__ __forceinline__ v4i ld_global16(const uint8_t* ptr) {
   return *reinterpret_cast<const v4i*>(ptr);
+}
+// 16-byte buffer load of lane offset voff from a wave-uniform base whose valid range is nrec
+// bytes: offsets at or past nrec return zeros without a memory access. The base and range are
+// made explicitly uniform so they live in scalar registers. Non-temporal cache policy.
+__device__ __forceinline__ v4i ld_buffer16_nt(const uint8_t* base, int nrec, uint32_t voff) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint8_t* ub = reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2));
+}
+// Streaming load (non-temporal hint): for data read exactly once, like decode's K/V.
+__device__ __forceinline__ v4i ld_global16_nt(const uint8_t* ptr) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4i*>(ptr));
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
@@ -138,6 +160,10 @@ __device__ __forceinline__ SeqInfo seq_info(const KParams& p, int b) {
   if (p.used_k) s.sk = p.used_k[b];
   else if (p.cu_k) s.sk = p.cu_k[b + 1] - p.cu_k[b];
   else s.sk = p.max_sk;
+  // b is uniform: keep the lengths in scalar registers (the loads above may be vector loads)
+  s.q0 = __builtin_amdgcn_readfirstlane(s.q0);
+  s.sq = __builtin_amdgcn_readfirstlane(s.sq);
+  s.sk = __builtin_amdgcn_readfirstlane(s.sk);
   return s;
 }
 
@@ -583,13 +609,21 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
 // no branches around its loads, so the compiler's in-order vector-memory wait counts stay
 // exact. Contiguous K/V is PAGEMODE 0.
 // ------------------------------------------------------------------------------------------
-// Waves per SIMD the decode kernel is compiled for: two when its registers fit in 256.
+// Tiles a decode wave keeps in flight in registers (one wave per SIMD, so the whole 512-entry
+// register file is available: DEPTH x (d + dv) / 4 registers of staging).
+// Two stages measured faster than three or four on the paged GQA decode workload (the extra
+// requests in flight only lengthen the memory queues).
 template <int D, int DV, int NQB>
-constexpr int decode_waves() { return (NQB == 1 && D + DV <= 256) ? 2 : 1; }
+constexpr int decode_depth() {
+  if (D + DV <= 256) return 2;
+  if (D + DV >= 512 || NQB == 2) return 1;   // two stages would spill
+  return 2;
+}
 
 template <int D, int DV, int NQB, int PAGEMODE>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(decode_waves<D, DV, NQB>(), 8)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa8_decode_kernel(const KParams p) {
+  constexpr int DEPTH = decode_depth<D, DV, NQB>();
   constexpr int BN = kKvTile;
   constexpr int KCH = D / 16, VCH = DV / 16;
   constexpr int KTILE = BN * D, VTILE = BN * DV;
@@ -668,55 +702,107 @@ fa8_decode_kernel(const KParams p) {
 
   const KvAddr ka = kv_addr(p, b, kvh);
   const int jlast = si.sk - 1;
-  int win_base = 0, win_val = 0;
-
-  // 16-byte chunk (row, ch) of tile j0, load instruction with first row j0 + r0. The row is
-  // clamped to the last valid one: rows past the sequence are masked to P = 0 and the clamped V
-  // row is finite, so they contribute exactly 0.
-  auto chunk_ptr = [&](const uint8_t* base_ptr, int64_t kvbase, int64_t pstride, int64_t rstride, int j0, int r0,
-                       int row, int ch) -> const uint8_t* {
-    const int j = min(j0 + row, jlast);
-    if constexpr (PAGEMODE == 0) {
-      const uint8_t* base = base_ptr + kvbase + (int64_t)j0 * rstride;          // uniform
-      return base + (uint32_t)((j - j0) * (int)rstride + ch * 16);
-    } else if constexpr (PAGEMODE == 1) {
-      const int jr = min(j0 + r0, jlast);
-      const int page = __builtin_amdgcn_readlane(win_val, (jr >> ka.shift) - win_base);
-      const uint8_t* base = base_ptr + kvbase + (int64_t)page * pstride;       // uniform
-      return base + (uint32_t)((j & ka.pmask) * (int)rstride + ch * 16);
-    } else {
-      const int page = __shfl(win_val, (j >> ka.shift) - win_base);
-      return base_ptr + kvbase + (int64_t)page * pstride + (int64_t)(j & ka.pmask) * rstride + ch * 16;
+  // Rows of one 64-lane load instruction: 64 / NCH (they lie in one page under PAGEMODE 1).
+  constexpr int KRPI = (64 % KCH == 0) ? 64 / KCH : 1, VRPI = (64 % VCH == 0) ? 64 / VCH : 1;
+  static_assert(PAGEMODE != 1 || (64 % KCH == 0 && 64 % VCH == 0), "PAGEMODE 1 needs whole rows per load");
+  // Block-table window (paged): lane i describes page win_base + i (clamped to the sequence's
+  // last page). PAGEMODE 1 keeps the address of that page's K and V rows of this kv head as
+  // 32-bit halves; PAGEMODE 2 keeps the page number.
+  int win_base = 0, win_pg = 0;
+  uint32_t wk_lo = 0, wk_hi = 0, wv_lo = 0, wv_hi = 0;
+  auto load_window = [&](int base) {
+    win_base = base;
+    win_pg = ka.trow[min(win_base + lane, jlast >> ka.shift)];
+    if constexpr (PAGEMODE == 1) {
+      const uint64_t ko = reinterpret_cast<uint64_t>(p.k + (int64_t)win_pg * ka.k_ps + ka.kbase);
+      const uint64_t vo = reinterpret_cast<uint64_t>(p.v + (int64_t)win_pg * ka.v_ps + ka.vbase);
+      wk_lo = (uint32_t)ko; wk_hi = (uint32_t)(ko >> 32);
+      wv_lo = (uint32_t)vo; wv_hi = (uint32_t)(vo >> 32);
     }
   };
-  v4i kr[KPT], vr[VPT];
-  auto gload = [&](int t) {
+  // Per-lane byte offset inside a load instruction's rows when 64 / NCH whole rows make one
+  // instruction: row lane / NCH of the instruction, chunk lane % NCH (the same for every
+  // instruction and tile).
+  const uint32_t lane_off_k = (uint32_t)((lane / KCH) * (int)ka.k_rs + (lane % KCH) * 16);
+  const uint32_t lane_off_v = (uint32_t)((lane / VCH) * (int)ka.v_rs + (lane % VCH) * 16);
+
+  // This lane's 16-byte chunk of load instruction u of the tile starting at key j0.
+  // PAGEMODE 0 and 1 use buffer loads whose range (num_records) ends at the sequence's last key:
+  // chunks of rows past it return zeros without a memory access, and a step past the window
+  // end (real == false) gets an empty range, so all of its loads return zeros and cost no
+  // memory traffic. (Contiguous rows and page rows at most 64 rows x row stride < 2^31 bytes
+  // from the base, checked on the host.)
+  // PAGEMODE 1: an instruction's rows lie in one page (page_size >= rows per instruction, both
+  // powers of two), so its base is uniform: the window's page offset + the in-page row offset.
+  // PAGEMODE 2 (pages smaller than one instruction's rows): per-lane page lookup by a lane
+  // shuffle, rows clamped to the last valid key, and a filler step reads a small cached block.
+  auto chunk_load = [&](bool is_v, int j0, int u, bool real) -> v4i {
+    const int NCH = is_v ? VCH : KCH;
+    const int rpi = is_v ? VRPI : KRPI;
+    const int rs = (int)(is_v ? ka.v_rs : ka.k_rs);
+    const uint8_t* base_ptr = is_v ? p.v : p.k;
+    if constexpr (PAGEMODE == 1) {
+      const int jr = j0 + u * rpi;                                               // uniform
+      const int idx = min((jr >> ka.shift) - win_base, 63);
+      const uint32_t lo = __builtin_amdgcn_readlane(is_v ? wv_lo : wk_lo, idx);
+      const uint32_t hi = __builtin_amdgcn_readlane(is_v ? wv_hi : wk_hi, idx);
+      const uint8_t* base = reinterpret_cast<const uint8_t*>((((uint64_t)hi) << 32) | lo) +
+                            (uint32_t)((jr & ka.pmask) * rs);   // uniform
+      const int rem = si.sk - jr;   // rows of this instruction that are keys of the sequence
+      const int nrec = (real && rem > 0) ? min(rem, rpi) * rs : 0;
+      return ld_buffer16_nt(base, nrec, is_v ? lane_off_v : lane_off_k);
+    } else if constexpr (PAGEMODE == 0) {
+      const int64_t kvbase = is_v ? ka.vbase : ka.kbase;
+      if ((is_v ? VRPI : KRPI) * NCH == 64) {
+        // whole rows per instruction: uniform base at the instruction's first row
+        const int jr = j0 + u * rpi;
+        const uint8_t* base = base_ptr + kvbase + (int64_t)jr * rs;
+        const int rem = si.sk - jr;
+        const int nrec = (real && rem > 0) ? min(rem, rpi) * rs : 0;
+        return ld_buffer16_nt(base, nrec, is_v ? lane_off_v : lane_off_k);
+      } else {
+        const int cid = u * 64 + lane;
+        const int row = cid / NCH, ch = cid - row * NCH;
+        const uint8_t* base = base_ptr + kvbase + (int64_t)j0 * rs;
+        const int rem = si.sk - j0;
+        const int nrec = (real && rem > 0) ? min(rem, BN) * rs : 0;
+        return ld_buffer16_nt(base, nrec, (uint32_t)(row * rs + ch * 16));
+      }
+    } else {
+      const int cid = u * 64 + lane;
+      const int row = cid / NCH, ch = cid - row * NCH;
+      const int j = min(j0 + row, jlast);
+      const int page = __shfl(win_pg, (j >> ka.shift) - win_base);
+      const uint8_t* ptr = base_ptr + (is_v ? ka.vbase : ka.kbase) + (int64_t)page * (is_v ? ka.v_ps : ka.k_ps) +
+                           (int64_t)(j & ka.pmask) * rs + ch * 16;
+      return ld_global16_nt(real ? ptr : g_filler + lane * 16);
+    }
+  };
+  v4i kr[DEPTH][KPT], vr[DEPTH][VPT];
+  // Loads of tile t into one register stage. A step past the window end (real == false)
+  // issues the same loads, which then return zeros (or read the filler block): every step
+  // issues the same loads, so the compiler's in-order wait counts are exact and each tile's
+  // wait leaves the DEPTH-1 younger tiles in flight.
+  auto gload = [&](int t, bool real, v4i (&ks)[KPT], v4i (&vs)[VPT]) {
     const int j0 = t * BN;
 #pragma unroll
-    for (int u = 0; u < KPT; u++) {
-      const int cid = u * 64 + lane;
-      const int row = cid / KCH, ch = cid - row * KCH;
-      kr[u] = ld_global16(chunk_ptr(p.k, ka.kbase, ka.k_ps, ka.k_rs, j0, (u * 64) / KCH, row, ch));
-    }
+    for (int u = 0; u < KPT; u++) ks[u] = chunk_load(false, j0, u, real);
 #pragma unroll
-    for (int u = 0; u < VPT; u++) {
-      const int cid = u * 64 + lane;
-      const int row = cid / VCH, ch = cid - row * VCH;
-      vr[u] = ld_global16(chunk_ptr(p.v, ka.vbase, ka.v_ps, ka.v_rs, j0, (u * 64) / VCH, row, ch));
-    }
+    for (int u = 0; u < VPT; u++) vs[u] = chunk_load(true, j0, u, real);
   };
-  auto swrite = [&]() {
+  // Registers -> LDS (swizzled rows).
+  auto swrite = [&](v4i (&ks)[KPT], v4i (&vs)[VPT]) {
 #pragma unroll
     for (int u = 0; u < KPT; u++) {
       const int cid = u * 64 + lane;
       const int row = cid / KCH, ch = cid - row * KCH;
-      *reinterpret_cast<v4i*>(smem + row * D + swz<KCH>(ch, k_sv(row)) * 16) = kr[u];
+      *reinterpret_cast<v4i*>(smem + row * D + swz<KCH>(ch, k_sv(row)) * 16) = ks[u];
     }
 #pragma unroll
     for (int u = 0; u < VPT; u++) {
       const int cid = u * 64 + lane;
       const int row = cid / VCH, ch = cid - row * VCH;
-      *reinterpret_cast<v4i*>(smem + KTILE + row * DV + swz<VCH>(ch, v_sv16(row)) * 16) = vr[u];
+      *reinterpret_cast<v4i*>(smem + KTILE + row * DV + swz<VCH>(ch, v_sv16(row)) * 16) = vs[u];
     }
   };
 
@@ -731,31 +817,48 @@ fa8_decode_kernel(const KParams p) {
   }
 
   const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem;
-  // Tiles [w0, w1): tile t goes registers -> LDS, then tile t+1's loads are issued (a scheduling
-  // barrier keeps them ahead of the compute), then tile t is computed from LDS.
-  auto run_tiles = [&](int w0, int w1) {
-    gload(w0);
-    for (int t = w0; t < w1; t++) {
-      wave_lds_order();   // the previous tile's LDS reads are issued before these writes
-      swrite();
-      wave_lds_order();
-      if (t + 1 < w1) gload(t + 1);
-      __builtin_amdgcn_sched_barrier(0);
+  // Tiles [w0, w1) with DEPTH register stages: tile t (stage t mod DEPTH) goes registers -> LDS,
+  // then tile t+DEPTH's loads reuse that stage (a scheduling barrier keeps them ahead of the
+  // compute), then tile t is computed from LDS; DEPTH tiles are always in flight. Steps past w1
+  // run with dummy loads and no compute, so loads and waits never sit under a branch.
+  auto step = [&](auto stage, int t, int w1) {
+    constexpr int st = decltype(stage)::value;
+    wave_lds_order();   // the previous tile's LDS reads are issued before these writes
+    swrite(kr[st], vr[st]);
+    wave_lds_order();
+    gload(t + DEPTH, t + DEPTH < w1, kr[st], vr[st]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < w1) {
       const int j0 = t * BN;
       const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
       attn_tile16<D, DV, NQB>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+    }
+  };
+  auto run_tiles = [&](int w0, int w1) {
+    // issue order = consumption order, so each tile's wait leaves the later tiles in flight
+    gload(w0, true, kr[0], vr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DEPTH > 1) gload(w0 + 1, w0 + 1 < w1, kr[1 % DEPTH], vr[1 % DEPTH]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DEPTH > 2) gload(w0 + 2, w0 + 2 < w1, kr[2 % DEPTH], vr[2 % DEPTH]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (DEPTH > 3) gload(w0 + 3, w0 + 3 < w1, kr[3 % DEPTH], vr[3 % DEPTH]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = w0; t < w1; t += DEPTH) {
+      step(std::integral_constant<int, 0>{}, t, w1);
+      if constexpr (DEPTH > 1) step(std::integral_constant<int, 1 % DEPTH>{}, t + 1, w1);
+      if constexpr (DEPTH > 2) step(std::integral_constant<int, 2 % DEPTH>{}, t + 2, w1);
+      if constexpr (DEPTH > 3) step(std::integral_constant<int, 3 % DEPTH>{}, t + 3, w1);
     }
   };
 
   if constexpr (PAGEMODE == 0) {
     if (t_begin < t_end) run_tiles(t_begin, t_end);
   } else {
-    const int last_page = jlast >> ka.shift;
     int t = t_begin;
     while (t < t_end) {
       // window of 64 entries from this tile's first page; then the tiles whose rows all fall in it
-      win_base = (t * BN) >> ka.shift;
-      win_val = ka.trow[min(win_base + lane, last_page)];
+      load_window((t * BN) >> ka.shift);
       wait_vmcnt<0>();
       int w1 = t + 1;
       while (w1 < t_end && ((min(w1 * BN + BN - 1, jlast) >> ka.shift) - win_base) < 64) w1++;
@@ -839,12 +942,17 @@ static void launch_decode_q(const KParams& kp, dim3 grid, hipStream_t stream) {
   // the rows of one 64-lane load instruction (64 / (d/16) rows) lie in one page
   constexpr int rows_k = (64 % (D / 16) == 0) ? 64 / (D / 16) : 1 << 30;
   constexpr int rows_v = (64 % (DV / 16) == 0) ? 64 / (DV / 16) : 1 << 30;
-  if (kp.page_shift < 0)
+  if (kp.page_shift < 0) {
     hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 0>), grid, dim3(64), 0, stream, kp);
-  else if ((1 << kp.page_shift) >= rows_k && (1 << kp.page_shift) >= rows_v)
-    hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 1>), grid, dim3(64), 0, stream, kp);
-  else
-    hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 2>), grid, dim3(64), 0, stream, kp);
+    return;
+  }
+  if constexpr (rows_k < (1 << 30) && rows_v < (1 << 30)) {
+    if ((1 << kp.page_shift) >= rows_k && (1 << kp.page_shift) >= rows_v) {
+      hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 1>), grid, dim3(64), 0, stream, kp);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 2>), grid, dim3(64), 0, stream, kp);
 }
 template <int D, int DV>
 static hipError_t launch_decode_t(const KParams& kp, hipStream_t stream) {

@@ -174,23 +174,25 @@ def test_decode_partials_match_oracle_ranges():
         assert np.abs(gl[fin] - rl[fin]).max() <= 0.0646, f"partial lse split {s}"
 
 
-def test_decode_empty_and_poisoned_pages():
+@pytest.mark.parametrize("d,page", [(128, 16), (128, 64), (128, 8), (128, 4), (64, 16), (256, 16), (96, 16)])
+def test_decode_empty_and_poisoned_pages(d, page):
     # a zero-length sequence and NaN-filled unused pages / tail slots must not reach the output
-    inp = gen.make_paged(31, [0, 33, 200, 16], 8, 2, 128, 128, page_size=16, sq=1, varlen_q=True)
+    # (page sizes at, above and below the rows one 64-lane load covers: 64 / (d / 16))
+    inp = gen.make_paged(31, [0, 33, 200, 16, 129], 8, 2, d, d, page_size=page, sq=1, varlen_q=True)
     used = set()
     for b, s in enumerate(inp.seqused_k):
-        used.update(inp.block_table[b, : (int(s) + 15) // 16].tolist())
+        used.update(inp.block_table[b, : (int(s) + page - 1) // page].tolist())
     for pg in range(inp.k.shape[0]):
         if pg not in used:
             inp.k[pg] = 0x7F
             inp.v[pg] = 0x7F
     for b, s in enumerate(inp.seqused_k):
         s = int(s)
-        if s % 16:
-            pg = inp.block_table[b, s // 16]
-            inp.k[pg, s % 16:] = 0x7F
-            inp.v[pg, s % 16:] = 0x7F
-    got = _decode_check(inp, 3, "decode with poison")
+        if s % page:
+            pg = inp.block_table[b, s // page]
+            inp.k[pg, s % page:] = 0x7F
+            inp.v[pg, s % page:] = 0x7F
+    got = _decode_check(inp, 3, f"decode with poison d{d} page{page}")
     assert np.all(got[0] == 0)
 
 
