@@ -99,7 +99,7 @@ def device_args(inp, dev):
 def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None):
     q, k, v, kw = device_args(inp, dev)
     B, HQ, SQ, DV = inp.batch, inp.heads_q, inp.max_seqlen_q, inp.dv
-    S = num_splits or binding.decode_num_splits(B, inp.heads_kv, inp.max_seqlen_k)
+    S = num_splits or binding.decode_num_splits_for(q, k, v, **kw)
     op = torch.empty((S, B, SQ, HQ, DV), dtype=torch.float32, device=dev)
     lp = torch.empty((S, B, SQ, HQ), dtype=torch.float32, device=dev)
     out = torch.empty((q.shape[0], HQ, DV), dtype=torch.bfloat16, device=dev)
@@ -264,7 +264,7 @@ def main():
                    "d": dec.d, "page_size": dec.page_size, "seqlens_k": "uniform [1024, 8192], seed 1",
                    "sum_seqlen_k": int(dec.seqlens_k().sum()), "num_splits": S, "out": "bf16",
                    "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": "fa8_decode_kernel<128,128,1,1> (split-KV decode, paged)",
+        "roofline": {"bound": "hbm", "kernel": "fa8_decode_rows_kernel<128,128,4,2> (split-KV decode, paged, whole rows)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel_ms": round(kern_ms, 5), "bytes_per_launch": kbytes},

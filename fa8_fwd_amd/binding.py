@@ -30,6 +30,11 @@ class Descale(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
 
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("block_keys", ctypes.c_int32), ("key_groups", ctypes.c_int32),
+                ("heads_per_workgroup", ctypes.c_int32), ("workgroups", ctypes.c_int64)]
+
+
 class FwdParams(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
@@ -78,6 +83,10 @@ def load():
         getattr(lib, f).restype = ctypes.c_int
     lib.fa8_decode_num_splits.argtypes = [i32, i32, i32, i32]
     lib.fa8_decode_num_splits.restype = i32
+    lib.fa8_decode_plan.argtypes = [P, i32, ctypes.POINTER(DecodePlan)]
+    lib.fa8_decode_plan.restype = ctypes.c_int
+    lib.fa8_decode_num_splits_for.argtypes = [P, i32]
+    lib.fa8_decode_num_splits_for.restype = i32
     lib.fa8_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.fa8_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa8_last_error.restype = ctypes.c_char_p
@@ -253,6 +262,23 @@ def decode_num_splits(batch: int, heads_kv: int, max_seqlen_k: int, cu_count: in
     return int(load().fa8_decode_num_splits(batch, heads_kv, max_seqlen_k, cu_count))
 
 
+def decode_num_splits_for(q, k, v, *, cu_count: int = 0, **kw) -> int:
+    """Split count the library picks for this decode problem (fa8_decode_num_splits_for)."""
+    p = _params(q, k, v, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
+                kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), None, None, None, 0.0, False, -1, -1)
+    return int(load().fa8_decode_num_splits_for(ctypes.byref(p), cu_count))
+
+
+def decode_plan(q, k, v, *, num_splits: int, **kw) -> dict:
+    """How fa8_fwd_decode_splitkv computes this problem (fa8_decode_plan): kernel, block_keys,
+    key_groups, heads_per_workgroup, workgroups."""
+    p = _params(q, k, v, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
+                kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), None, None, None, 0.0, False, -1, -1)
+    info = DecodePlan()
+    _check(load().fa8_decode_plan(ctypes.byref(p), num_splits, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in DecodePlan._fields_}
+
+
 def decode_workspace_bytes(num_splits: int, batch: int, max_seqlen_q: int, heads_q: int, dv: int) -> int:
     return int(load().fa8_decode_workspace_bytes(num_splits, batch, max_seqlen_q, heads_q, dv))
 
@@ -305,12 +331,12 @@ def combine(o_partial, lse_partial, *, batch: int, max_seqlen_q: int, heads_q: i
 
 def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=torch.bfloat16, return_lse=False,
            workspace: Optional[torch.Tensor] = None, stream=None, **kw):
-    """Split-KV decode followed by the combine. num_splits=None uses fa8_decode_num_splits."""
+    """Split-KV decode followed by the combine. num_splits=None uses fa8_decode_num_splits_for."""
     cu_q = kw.get("cu_seqlens_q")
     p = _params(q, k, v, cu_q, kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
                 kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), None, None, None, 0.0, False, -1, -1)
     if num_splits is None:
-        num_splits = decode_num_splits(p.batch, p.heads_kv, p.max_seqlen_k)
+        num_splits = int(load().fa8_decode_num_splits_for(ctypes.byref(p), 0))
     S, B, SQ, HQ, DV = num_splits, p.batch, p.max_seqlen_q, p.heads_q, p.dv
     op = lp = None
     if workspace is not None:

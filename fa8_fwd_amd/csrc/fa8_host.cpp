@@ -231,6 +231,51 @@ int32_t fa8_decode_num_splits(int32_t batch, int32_t heads_kv, int32_t max_seqle
   return (int32_t)s;
 }
 
+int32_t fa8_decode_num_splits_for(const fa8_fwd_params* p, int32_t cu_count) {
+  if (!p || validate(p, 1) != FA8_OK) return 1;
+  if (cu_count <= 0) cu_count = 256;
+  if (p->batch <= 0 || p->heads_kv <= 0 || p->max_seqlen_k <= 0 || p->max_seqlen_q <= 0) return 1;
+  fa8::KParams k = make_kparams(p);
+  const int64_t rows = (int64_t)p->max_seqlen_q * k.g;
+  k.nmb = (int32_t)((rows + fa8::kDecodeRows - 1) / fa8::kDecodeRows);
+  const int64_t units = std::max<int64_t>(1, fa8::decode_units_per_split(k, p->d, p->dv));
+  // one-wave workgroups. Several-heads kernel: about one wave per SIMD (more concurrent streams
+  // measured slower); per-head kernel: about four per SIMD (measured best at the paged GQA
+  // decode shape)
+  const bool heads = fa8::decode_heads_choice(k, p->d, p->dv) != 0;
+  const int64_t target = (int64_t)cu_count * (heads ? 4 : 16);
+  const int64_t granules = ((int64_t)p->max_seqlen_k + FA8_SPLIT_GRANULE - 1) / FA8_SPLIT_GRANULE;
+  int64_t s = (target + units - 1) / units;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, granules / 4));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, FA8_MAX_SPLITS));
+  return (int32_t)s;
+}
+
+fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_decode_plan_info* info) {
+  if (!info) return fail(FA8_ERR_INVALID, "info must be non-NULL");
+  if (num_splits < 1) return fail(FA8_ERR_INVALID, "num_splits must be >= 1 (got %d)", num_splits);
+  fa8_status st = validate(p, num_splits);
+  if (st != FA8_OK) return st;
+  fa8::KParams k = make_kparams(p);
+  k.nsplit = num_splits;
+  const int64_t rows = (int64_t)p->max_seqlen_q * k.g;
+  k.nmb = (int32_t)((rows + fa8::kDecodeRows - 1) / fa8::kDecodeRows);
+  const int hpw = fa8::decode_heads_choice(k, p->d, p->dv);
+  if (hpw) {
+    info->kernel = 1;
+    info->block_keys = 64 / hpw;
+    info->key_groups = 1;
+    info->heads_per_workgroup = hpw;
+  } else {
+    info->kernel = 0;
+    info->block_keys = fa8::kKvTile;
+    info->key_groups = 1;
+    info->heads_per_workgroup = 1;
+  }
+  info->workgroups = (int64_t)fa8::decode_units_per_split(k, p->d, p->dv) * num_splits;
+  return ok();
+}
+
 size_t fa8_decode_workspace_bytes(int32_t num_splits, int32_t batch, int32_t max_seqlen_q, int32_t heads_q,
                                   int32_t dv) {
   if (num_splits < 0 || batch < 0 || max_seqlen_q < 0 || heads_q < 0 || dv < 0) return 0;

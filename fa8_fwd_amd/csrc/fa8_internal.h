@@ -46,6 +46,11 @@ constexpr int kPrefillRows = 128;
 constexpr int kDecodeRows = 32;
 constexpr int kKvTile = 64;
 
+// kv heads per wave of the several-heads decode kernel, or 0 when the per-head kernel is used.
+int decode_heads_choice(const KParams& kp, int d, int dv);
+// Workgroups per split of the decode kernel launch_decode picks.
+int decode_units_per_split(const KParams& kp, int d, int dv);
+
 hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_combine(const CParams& cp, hipStream_t stream);

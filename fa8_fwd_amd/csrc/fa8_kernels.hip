@@ -30,6 +30,7 @@
 //    the rows that one LDS read instruction touches fall in distinct banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <type_traits>
 
@@ -109,6 +110,34 @@ __device__ __forceinline__ v4i ld_buffer16_nt(const uint8_t* base, int nrec, uin
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2));
+}
+// Cross-lane moves within a wave through the gfx950 permlane swaps (VALU, no LDS round trip).
+// permlane16_swap(x, x) leaves {x of row 2k, x of row 2k+1} in both rows of each pair of
+// 16-lane rows, permlane32_swap(x, x) leaves {x of rows 0-1, x of rows 2-3} in both halves.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// the value x of lane ^ 16 / lane ^ 32
+__device__ __forceinline__ uint32_t from_xor16(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return ((lane >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t from_xor32(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (lane >> 5) ? r[0] : r[1];
 }
 // Streaming load (non-temporal hint): for data read exactly once, like decode's K/V.
 __device__ __forceinline__ v4i ld_global16_nt(const uint8_t* ptr) {
@@ -886,6 +915,381 @@ fa8_decode_kernel(const KParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Split-KV decode with several kv heads per wave, for GQA shapes with few query rows per kv
+// head: one wave per (group of HPW kv heads, split, batch). The Sq*g rows of each of the HPW
+// heads together fill the 16 rows of one 16x16 MFMA block (HPW * Sq * g <= 16), so no MFMA row
+// is padding. A step covers BN = 64 / HPW keys of all HPW heads (16 KB at d = dv = 128), loaded
+// into registers as whole token rows of the group (the HPW heads of a token are HPW * d
+// contiguous bytes) and staged through one LDS stage, with the pipeline of the per-head kernel.
+//   S^T (16 keys x 16 rows) of key block kb: sum over heads a of K_a . Q_a'^T, where Q_a' is Q
+//     with the rows of the other heads zeroed, so every row only sees its own head's keys.
+//   O^T (16 dv x 16 rows) of a step: one 16x16x128 MFMA per 16 dv columns. Its 128 K slots are
+//     four groups of 32; group kg belongs to (head a = kg / KB, key block kb = kg % KB) and holds
+//     that block's 16 keys (16 slots, the rest zero). Row r's P enters only the groups of r's
+//     own head, so the sum over all slots is exactly sum_j P[r][j] V_head(r)[j].
+// ------------------------------------------------------------------------------------------
+// PAGED: K/V through the block table; STEP_PAGE: page_size >= BN, so each step's rows lie in
+// one page (or K/V are contiguous) and one descriptor per step serves all of its loads.
+template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa8_decode_heads_kernel(const KParams p) {
+  static_assert(HPW == 2 || HPW == 4, "two or four kv heads per wave");
+  constexpr int KB = 4 / HPW;                        // 16-key blocks per step
+  constexpr int BN = 16 * KB;                        // keys per step
+  constexpr int KR = HPW * D, VR = HPW * DV;         // bytes of one token's K / V row for the heads
+  static_assert(KR <= 1024 && VR <= 1024, "a load instruction holds whole rows");
+  constexpr int KLPR = KR / 16, VLPR = VR / 16;      // lanes per row in a load instruction
+  constexpr int KRPI = 64 / KLPR, VRPI = 64 / VLPR;  // rows per load instruction
+  constexpr int KPT = BN / KRPI, VPT = BN / VRPI;    // load instructions per step
+  constexpr int KTILE = BN * KR, VTILE = BN * VR;
+  constexpr int KSW = (KLPR < 16 ? KLPR : 16) - 1, VSW = (VLPR < 16 ? VLPR : 16) - 1;   // swizzle masks
+  constexpr int KS = (D + 127) / 128;
+  constexpr int NB = DV / 16;
+  constexpr int DEPTH = 1;   // one register stage + the LDS stage; two waves per SIMD overlap
+  __shared__ __attribute__((aligned(16))) uint8_t smem[KTILE + VTILE];
+
+  const int lane = threadIdx.x;
+  const int kg = lane >> 4, l16 = lane & 15;
+  const int b = blockIdx.z, split = blockIdx.y;
+  const int kvh0 = blockIdx.x * HPW;
+  const int g = p.g;
+  const SeqInfo si = seq_info(p, b);
+  const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+
+  // ---- key range of the wave (all query tokens of the batch) and of this split ----
+  int wg_lo = 0, wg_hi = 0, full_lo = 0, full_hi = 0;
+  if (si.sq > 0) {
+    wg_lo = rr.lo(0);
+    wg_hi = rr.hi(si.sq - 1);
+    full_lo = rr.lo(si.sq - 1);
+    full_hi = rr.hi(0);
+  }
+  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
+  {
+    // split s covers granules [g0 + s*n/S, g0 + (s+1)*n/S) of the block's granule range
+    const int g0 = wg_lo / kKvTile, g1 = (wg_hi + kKvTile - 1) / kKvTile, n = g1 - g0;
+    const int s0 = g0 + (int)(((int64_t)split * n) / p.nsplit);
+    const int s1 = g0 + (int)(((int64_t)(split + 1) * n) / p.nsplit);
+    wg_lo = max(wg_lo, s0 * kKvTile);
+    wg_hi = min(wg_hi, s1 * kKvTile);
+    full_lo = max(full_lo, s0 * kKvTile);
+    full_hi = min(full_hi, s1 * kKvTile);
+  }
+  const int t_begin = wg_lo / BN;
+  const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
+
+  // ---- this lane's row: head slot a, query token qi, q head qg of the group ----
+  const int rp = p.max_sq * g;                       // rows per kv head (host: HPW * rp <= 16)
+  const int my_a = l16 / rp, rq = l16 - my_a * rp;
+  const int qi = rq / g, qg = rq - qi * g;
+  const bool valid = my_a < HPW && qi < si.sq;
+  const int kvh = kvh0 + min(my_a, HPW - 1);
+  const int qh = kvh * g + qg;
+  const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
+  const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
+  const float dvs = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh);
+  const float c = p.scale_log2 * dq * dk;
+  int my_lo = 0, my_hi = 0;
+  if (valid) {
+    my_lo = max(rr.lo(qi), wg_lo);
+    my_hi = min(rr.hi(qi), wg_hi);
+  }
+
+  // Q of this row as the B operand (d-bytes [128ks + 32kg, +32)), once per head slot with the
+  // other slots' rows zeroed
+  v8i qm[HPW][KS];
+  {
+    const uint8_t* qrow = p.q + (p.cu_q ? (int64_t)(si.q0 + qi) * p.q_rs : (int64_t)b * p.q_bs + (int64_t)qi * p.q_rs) +
+                          (int64_t)qh * p.q_hs;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int off = ks * 128 + kg * 32;
+      v4i x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+      if (valid && off < D) {
+        x0 = ld_global16(qrow + off);
+        x1 = ld_global16(qrow + off + 16);
+      }
+      const v8i q8 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+      for (int a = 0; a < HPW; a++) qm[a][ks] = (a == my_a) ? q8 : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  // ---- K/V rows ----
+  const int shift = PAGED ? p.page_shift : 0, pmask = PAGED ? (1 << p.page_shift) - 1 : 0;
+  const int jlast = si.sk - 1;
+  const int k_rs = (int)p.k_rs, v_rs = (int)p.v_rs;   // row strides: page_size (or 64) rows < 2^31 bytes
+  const uint8_t* kbase = p.k + (int64_t)kvh0 * p.k_hs +
+                         (PAGED ? 0 : (p.cu_k ? (int64_t)p.cu_k[b] * p.k_rs : (int64_t)b * p.k_bs));
+  const uint8_t* vbase = p.v + (int64_t)kvh0 * p.v_hs +
+                         (PAGED ? 0 : (p.cu_k ? (int64_t)p.cu_k[b] * p.v_rs : (int64_t)b * p.v_bs));
+  // block-table window: lane i holds the K and V addresses of page win_base + i (clamped to the
+  // sequence's last page) for this group's first head, as 32-bit halves
+  int win_base = 0;
+  uint32_t wk_lo = 0, wk_hi = 0, wv_lo = 0, wv_hi = 0;
+  auto load_window = [&](int base) {
+    win_base = base;
+    const int pg = p.table[(int64_t)b * p.table_stride + min(win_base + lane, jlast >> shift)];
+    const uint64_t ka = reinterpret_cast<uint64_t>(kbase + (int64_t)pg * p.k_bs);
+    const uint64_t va = reinterpret_cast<uint64_t>(vbase + (int64_t)pg * p.v_bs);
+    wk_lo = (uint32_t)ka; wk_hi = (uint32_t)(ka >> 32);
+    wv_lo = (uint32_t)va; wv_hi = (uint32_t)(va >> 32);
+  };
+  // per-lane offset inside a load instruction: row lane / LPR of the instruction, chunk lane % LPR
+  const uint32_t lane_off_k = (uint32_t)((lane / KLPR) * k_rs + (lane % KLPR) * 16);
+  const uint32_t lane_off_v = (uint32_t)((lane / VLPR) * v_rs + (lane % VLPR) * 16);
+  // Load instruction u of the step at key j0: rows [j0 + u*RPI, +RPI), uniform base; a buffer
+  // range ending at the sequence's last key makes rows past it (and every load of a filler step,
+  // real == false) return zeros without a memory access. Paged: the rows of one instruction lie
+  // in one page (page_size >= rows per instruction, both powers of two).
+  auto chunk_load = [&](bool is_v, int j0, int u, bool real) -> v4i {
+    const int rpi = is_v ? VRPI : KRPI;
+    const int rs = is_v ? v_rs : k_rs;
+    const int jr = j0 + u * rpi;                                             // uniform
+    const uint8_t* base;
+    if constexpr (PAGED) {
+      const int idx = min((jr >> shift) - win_base, 63);
+      const uint32_t lo = __builtin_amdgcn_readlane(is_v ? wv_lo : wk_lo, idx);
+      const uint32_t hi = __builtin_amdgcn_readlane(is_v ? wv_hi : wk_hi, idx);
+      base = reinterpret_cast<const uint8_t*>((((uint64_t)hi) << 32) | lo) + (uint32_t)((jr & pmask) * rs);
+    } else {
+      base = (is_v ? vbase : kbase) + (int64_t)jr * rs;
+    }
+    const int rem = si.sk - jr;
+    const int nrec = (real && rem > 0) ? min(rem, rpi) * rs : 0;
+    return ld_buffer16_nt(base, nrec, is_v ? lane_off_v : lane_off_k);
+  };
+  // STEP_PAGE: the uniform base of the step's first row and the bytes of its rows that are keys
+  auto step_base = [&](bool is_v, int j0) -> const uint8_t* {
+    const int rs = is_v ? v_rs : k_rs;
+    if constexpr (PAGED) {
+      const int idx = min((j0 >> shift) - win_base, 63);
+      const uint32_t lo = __builtin_amdgcn_readlane(is_v ? wv_lo : wk_lo, idx);
+      const uint32_t hi = __builtin_amdgcn_readlane(is_v ? wv_hi : wk_hi, idx);
+      return reinterpret_cast<const uint8_t*>((((uint64_t)hi) << 32) | lo) + (uint32_t)((j0 & pmask) * rs);
+    } else {
+      return (is_v ? vbase : kbase) + (int64_t)j0 * rs;
+    }
+  };
+  v4i kr[DEPTH][KPT], vr[DEPTH][VPT];
+  auto gload = [&](int t, bool real, v4i (&ks)[KPT], v4i (&vs)[VPT]) {
+    const int j0 = t * BN;
+    if constexpr (STEP_PAGE) {
+      // one descriptor per step whose range is the step's key rows; instruction u adds its
+      // first row to the per-lane offset (the range check applies to the whole offset)
+      const int rem = si.sk - j0;
+      const int rows = (real && rem > 0) ? min(rem, BN) : 0;
+      const uint8_t* kb0 = step_base(false, j0);
+      const uint8_t* vb0 = step_base(true, j0);
+#pragma unroll
+      for (int u = 0; u < KPT; u++) ks[u] = ld_buffer16_nt(kb0, rows * k_rs, lane_off_k + (uint32_t)(u * KRPI * k_rs));
+#pragma unroll
+      for (int u = 0; u < VPT; u++) vs[u] = ld_buffer16_nt(vb0, rows * v_rs, lane_off_v + (uint32_t)(u * VRPI * v_rs));
+    } else {
+#pragma unroll
+      for (int u = 0; u < KPT; u++) ks[u] = chunk_load(false, j0, u, real);
+#pragma unroll
+      for (int u = 0; u < VPT; u++) vs[u] = chunk_load(true, j0, u, real);
+    }
+  };
+  // registers -> LDS: row r of the step at r*R, its 16-byte chunk c at position c ^ (r & SW)
+  auto swrite = [&](v4i (&ks)[KPT], v4i (&vs)[VPT]) {
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+      const int r = u * KRPI + lane / KLPR, ch = lane % KLPR;
+      *reinterpret_cast<v4i*>(smem + r * KR + ((ch ^ (r & KSW)) << 4)) = ks[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+      const int r = u * VRPI + lane / VLPR, ch = lane % VLPR;
+      *reinterpret_cast<v4i*>(smem + KTILE + r * VR + ((ch ^ (r & VSW)) << 4)) = vs[u];
+    }
+  };
+
+  // Two-level PV accumulation: oblk accumulates the PV products of up to four steps (64 keys)
+  // on the MFMA; it is folded into the fp32 oacc every fourth step, and before a step whose
+  // lazy rescale moves the running max of any row (then O = alpha (oacc + oblk) first).
+  float m_run = kNegInf, l_run = 0.0f;
+  v4f oacc[NB], oblk[NB];
+#pragma unroll
+  for (int n = 0; n < NB; n++) {
+    oacc[n] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    oblk[n] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  // PV operand geometry of this lane: K-slot group kg = (head ga, key block gb); dword j of the
+  // group holds keys 16 gb + 4 (kg ^ j) + [0, 4). The two transposed reads (e = 0, 1) give
+  // dwords 2e, 2e + 1; source lane s of a 16-lane group points at key byte s >> 1, column half
+  // s & 1 of the 16 dv columns.
+  const int ga = kg / KB, gb = kg % KB;
+  const bool my_group = (my_a == ga);
+  int tr_off[2];
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    const int byte = l16 >> 1;
+    const int row = 16 * gb + 4 * ((2 * e + (byte >> 2)) ^ kg) + (byte & 3);
+    tr_off[e] = row * VR + 8 * (l16 & 1);
+  }
+  const int tr_sw0 = (16 * gb + 4 * ((0 + ((l16 >> 1) >> 2)) ^ kg) + ((l16 >> 1) & 3)) & VSW;
+  const int tr_sw1 = (16 * gb + 4 * ((2 + ((l16 >> 1) >> 2)) ^ kg) + ((l16 >> 1) & 3)) & VSW;
+
+  const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem;
+  const FA8_LDS uint8_t* vt = kt + KTILE;
+  auto compute = [&](int t) {
+    const int j0 = t * BN;
+    const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+    // ---- S^T per key block ----
+    v4f sacc[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++) {
+      sacc[kb] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      const int krow = 16 * kb + l16;
+#pragma unroll
+      for (int a = 0; a < HPW; a++)
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+          const int off = ks * 128 + kg * 32;
+          v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (off < D) {
+            const int ch = (a * D + off) >> 4;
+            const v4i x0 = *(const FA8_LDS v4i*)(kt + krow * KR + ((ch ^ (krow & KSW)) << 4));
+            const v4i x1 = *(const FA8_LDS v4i*)(kt + krow * KR + (((ch + 1) ^ (krow & KSW)) << 4));
+            kop = (v8i){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          }
+          sacc[kb] = mfma_16x16x128_fp8(kop, qm[a][ks], sacc[kb]);
+        }
+    }
+    // ---- mask, row max (over the row's 4 lanes), lazy rescale, P ----
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int j = j0 + 16 * kb + 4 * kg + r;
+          if (j < my_lo || j >= my_hi) sacc[kb][r] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++)
+      mx = fmaxf(mx, fmaxf(fmaxf(sacc[kb][0], sacc[kb][1]), fmaxf(sacc[kb][2], sacc[kb][3])));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    const float mt = mx * c;
+    float alpha = 1.0f;
+    const bool moved = mt - m_run > kTau;
+    if (moved) {
+      alpha = fast_exp2(m_run - mt);
+      m_run = mt;
+    }
+    if (__builtin_amdgcn_ballot_w64(moved)) {   // uniform: fold before the scale changes
+#pragma unroll
+      for (int n = 0; n < NB; n++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          oacc[n][r] = alpha * (oacc[n][r] + oblk[n][r]);
+          oblk[n][r] = 0.0f;
+        }
+    }
+    const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
+    int pw[KB];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++) {
+      const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][0], c, nb));
+      const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][1], c, nb));
+      const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][2], c, nb));
+      const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][3], c, nb));
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+      pw[kb] = word;
+      const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+      const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
+      lsum += (r01[0] + r01[1]) + (r23[0] + r23[1]);
+    }
+    l_run = alpha * l_run + lsum;
+    // ---- P' (B operand): dword j of group kg = block gb's P of lane (row, kg ^ j) ----
+    // (lane ^ 16x sends the block the receiving lane's group needs: pw[(kg ^ x) % KB])
+    int pd[4];
+    pd[0] = pw[gb];
+    const uint32_t s1 = (uint32_t)pw[(kg ^ 1) % KB];
+    const uint32_t r1 = from_xor16(s1, lane);
+    pd[1] = (int)r1;
+    pd[2] = (int)from_xor32((uint32_t)pw[(kg ^ 2) % KB], lane);
+    pd[3] = (int)from_xor32(r1, lane);            // s1 of lane ^ 48 (pw[(kg ^ 3) % KB] == s1 there)
+    const v8i pop = my_group ? (v8i){pd[0], pd[1], pd[2], pd[3], 0, 0, 0, 0} : (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+    // ---- O^T of the step accumulated on the MFMA; fold every fourth step ----
+#pragma unroll
+    for (int n = 0; n < NB; n++) {
+      const int ch = ga * NB + n;
+      const v2i x0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + tr_off[0] + ((ch ^ tr_sw0) << 4)));
+      const v2i x1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + tr_off[1] + ((ch ^ tr_sw1) << 4)));
+      const v8i vop = {x0[0], x0[1], x1[0], x1[1], 0, 0, 0, 0};
+      oblk[n] = mfma_16x16x128_fp8(vop, pop, oblk[n]);
+    }
+    if ((t & 3) == 3) {
+#pragma unroll
+      for (int n = 0; n < NB; n++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          oacc[n][r] += oblk[n][r];
+          oblk[n][r] = 0.0f;
+        }
+    }
+  };
+
+  // Steps [w0, w1) with DEPTH register stages (as in the per-head kernel): step t goes registers
+  // -> LDS, step t+DEPTH's loads reuse that stage, then step t is computed from LDS.
+  auto step = [&](auto stage, int t, int w1) {
+    constexpr int st = decltype(stage)::value;
+    wave_lds_order();   // the previous step's LDS reads are issued before these writes
+    swrite(kr[st], vr[st]);
+    wave_lds_order();
+    gload(t + DEPTH, t + DEPTH < w1, kr[st], vr[st]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t < w1) compute(t);
+  };
+  auto run_steps = [&](int w0, int w1) {
+    gload(w0, true, kr[0], vr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int t = w0; t < w1; t += DEPTH) step(std::integral_constant<int, 0>{}, t, w1);
+  };
+  if constexpr (!PAGED) {
+    if (t_begin < t_end) run_steps(t_begin, t_end);
+  } else {
+    int t = t_begin;
+    while (t < t_end) {
+      // window of 64 entries from this step's first page; then the steps whose rows all fall in it
+      load_window((t * BN) >> shift);
+      wait_vmcnt<0>();
+      int w1 = t + 1;
+      while (w1 < t_end && ((min(w1 * BN + BN - 1, jlast) >> shift) - win_base) < 64) w1++;
+      run_steps(t, w1);
+      t = w1;
+    }
+  }
+
+#pragma unroll
+  for (int n = 0; n < NB; n++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) oacc[n][r] += oblk[n][r];
+  float l_tot = sum_xor16(l_run);
+  l_tot = sum_xor32(l_tot);
+  if (!valid) return;
+  const bool nonempty = l_tot > 0.0f;
+  const float inv = nonempty ? dvs / l_tot : 0.0f;
+  const float lse = nonempty ? (m_run + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
+  const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi) * p.hq + qh;
+  float* orow = p.o_part + prow * DV;
+#pragma unroll
+  for (int n = 0; n < NB; n++) {
+    const v4f v = {oacc[n][0] * inv, oacc[n][1] * inv, oacc[n][2] * inv, oacc[n][3] * inv};
+    *reinterpret_cast<v4f*>(orow + 16 * n + 4 * kg) = v;
+  }
+  if (kg == 0) p.lse_part[prow] = lse;
+}
+
 // Log-sum-exp merge of split partials: one thread per 4 output elements of one row.
 __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   const int tpr = c.dv / 4;
@@ -900,18 +1304,37 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   const int q0 = c.cu_q ? c.cu_q[b] : 0;
   const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
   if (i >= sq) return;
+  // splits in batches of 8 whose loads are all issued before any is used (the loop is bound by
+  // memory latency, not bandwidth)
+  constexpr int SB = 8;
   float mx = kNegInf;
-  for (int s = 0; s < c.nsplit; s++) mx = fmaxf(mx, c.lse_part[(int64_t)s * rows + row]);
+  for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
+    float ls[SB];
+#pragma unroll
+    for (int k = 0; k < SB; k++) ls[k] = (s0 + k < c.nsplit) ? c.lse_part[(int64_t)(s0 + k) * rows + row] : kNegInf;
+#pragma unroll
+    for (int k = 0; k < SB; k++) mx = fmaxf(mx, ls[k]);
+  }
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float den = 0.0f;
   if (mx != kNegInf) {
-    for (int s = 0; s < c.nsplit; s++) {
-      const float ls = c.lse_part[(int64_t)s * rows + row];
-      if (ls == kNegInf) continue;
-      const float w = __expf(ls - mx);
-      den += w;
-      const v4f o = *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)s * rows + row) * c.dv + 4 * q);
-      acc += w * o;
+    for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
+      float ls[SB];
+      v4f o[SB];
+#pragma unroll
+      for (int k = 0; k < SB; k++) {
+        const bool in = s0 + k < c.nsplit;
+        ls[k] = in ? c.lse_part[(int64_t)(s0 + k) * rows + row] : kNegInf;
+        o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)(s0 + k) * rows + row) * c.dv + 4 * q)
+                  : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int k = 0; k < SB; k++) {
+        // an empty split (LSE = -inf) has weight 0 and O = 0
+        const float w = (ls[k] == kNegInf) ? 0.0f : __expf(ls[k] - mx);
+        den += w;
+        acc += w * o[k];
+      }
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -979,8 +1402,59 @@ static hipError_t launch_decode_t(const KParams& kp, hipStream_t stream) {
 hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream) {
   FA8_DISPATCH(launch_prefill_t, d, dv, kp, stream);
 }
+// ---- several kv heads per wave: applicability and launch ----
+// Returns the kv heads per wave of fa8_decode_heads_kernel for this problem, or 0 when the
+// per-head kernel is used: (d, dv) in {(64, 64), (128, 128)}, the heads of a token row adjacent
+// in memory (head stride == head dim), 2 or 4 kv heads whose Sq * g rows fit one 16-row block,
+// and (paged) pages holding at least the rows of one 64-lane load. (Eight heads per wave, two
+// row blocks, measured slower: fewer waves and register spills.)
+int decode_heads_choice(const KParams& kp, int d, int dv) {
+  const char* env = getenv("FA8_DECODE_KERNEL");
+  if (env && env[0] == 'l') return 0;   // "lanes": force the per-head decode kernel
+  if (!((d == 64 && dv == 64) || (d == 128 && dv == 128))) return 0;
+  if (kp.k_hs != d || kp.v_hs != dv) return 0;
+  const int64_t rp = (int64_t)kp.max_sq * kp.g;
+  if (rp < 1 || rp > 8) return 0;
+  for (int hpw = (rp <= 4 ? 4 : 2); hpw >= 2; hpw /= 2) {
+    if (kp.hkv % hpw) continue;
+    const int rows_per_load = 1024 / (hpw * d);
+    if (kp.page_shift >= 0 && (1 << kp.page_shift) < rows_per_load) continue;
+    return hpw;
+  }
+  return 0;
+}
+
+template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE>
+static hipError_t launch_heads_t(const KParams& kp, hipStream_t stream) {
+  dim3 grid((unsigned)(kp.hkv / HPW), (unsigned)kp.nsplit, (unsigned)kp.batch);
+  hipLaunchKernelGGL((fa8_decode_heads_kernel<D, DV, HPW, PAGED, STEP_PAGE>), grid, dim3(64), 0, stream, kp);
+  return hipGetLastError();
+}
+
+// steps of 64 / H keys; a step lies in one page when the page holds at least that many rows
+#define FA8_HEADS_CASE(DD, H)                                                         \
+  if (d == DD && hpw == H) {                                                          \
+    if (kp.page_shift < 0) return launch_heads_t<DD, DD, H, false, true>(kp, stream); \
+    if ((1 << kp.page_shift) >= 64 / H) return launch_heads_t<DD, DD, H, true, true>(kp, stream); \
+    return launch_heads_t<DD, DD, H, true, false>(kp, stream);                      \
+  }
+
 hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream) {
+  const int hpw = decode_heads_choice(kp, d, dv);
+  if (hpw) {
+    FA8_HEADS_CASE(64, 2)
+    FA8_HEADS_CASE(64, 4)
+    FA8_HEADS_CASE(128, 2)
+    FA8_HEADS_CASE(128, 4)
+    return hipErrorInvalidValue;
+  }
   FA8_DISPATCH(launch_decode_t, d, dv, kp, stream);
+}
+
+int decode_units_per_split(const KParams& kp, int d, int dv) {
+  const int hpw = decode_heads_choice(kp, d, dv);
+  if (hpw) return kp.batch * (kp.hkv / hpw);
+  return kp.batch * kp.hkv * kp.nmb;
 }
 hipError_t launch_combine(const CParams& cp, hipStream_t stream) {
   const int64_t threads = (int64_t)cp.batch * cp.max_sq * cp.hq * (cp.dv / 4);

@@ -2,7 +2,7 @@
  * fa8.h: C ABI of an FP8 (E4M3) attention forward for AMD Instinct MI355X (gfx950).
  *
  * Computes O = softmax(Q K^T * scale) V with E4M3FN Q/K/V, an online softmax in exp2 with lazy
- * rescaling, P cast to E4M3 with a 2^8 bias, and two-level PV accumulation into fp32 O
+ * rescaling, P pre-scaled by 2^8 and rounded to E4M3, and two-level PV accumulation into fp32 O
  * ("[Cute,Fwd,Sm90] Native FP8 (E4M3 Q/K/V) forward for Hopper", Summary and Design; the
  * lazy-rescale bound log2(448) - 8 from "fp8 on the sheared forward", Correctness fix).
  *
@@ -64,7 +64,8 @@ typedef enum { FA8_OUT_BF16 = 0, FA8_OUT_FP16 = 1 } fa8_out_dtype;
  *   stride_b == stride_h == 0    -> one scalar *ptr
  *   otherwise                    -> ptr[b * stride_b + kv_head * stride_h] (fp32, device)
  * Q's descale is indexed by the KV head of the query head (kv_head = h / (heads_q / heads_kv)).
- * The q and k descales fold into the softmax scale, the v descale into the final normalization.
+ * Q and K descales multiply the softmax scale; the V descale multiplies the output after the
+ * softmax normalization.
  */
 typedef struct {
   const float* ptr;
@@ -175,11 +176,36 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
  * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything. Needs no GPU. */
 fa8_status fa8_check_params(const fa8_fwd_params* p, int32_t num_splits);
 
-/* Split count for fa8_fwd_decode_splitkv from host-known values only ("Launch choices depend
- * only on host-known values", Decode launches): enough (batch * heads_kv * splits) workgroups
+/* Split count for fa8_fwd_decode_splitkv computed from host-side values only, so that it holds
+ * under graph capture ("Native FP8 ... for Hopper", Design, Decode launches): enough (batch * heads_kv * splits) workgroups
  * to fill cu_count compute units, without splits shorter than a few granules. cu_count <= 0
  * means 256 (MI355X). Always returns 1 .. FA8_MAX_SPLITS. */
 int32_t fa8_decode_num_splits(int32_t batch, int32_t heads_kv, int32_t max_seqlen_k, int32_t cu_count);
+
+/* Split count for fa8_fwd_decode_splitkv on the problem p (host-side values only, graph-safe),
+ * for the decode kernel the library will pick for it: enough workgroups to keep cu_count compute
+ * units busy over a few rounds, without splits shorter than four granules. cu_count <= 0 means
+ * 256 (MI355X). Returns 1 .. FA8_MAX_SPLITS; 1 when p is NULL or fails validation. */
+int32_t fa8_decode_num_splits_for(const fa8_fwd_params* p, int32_t cu_count);
+
+/* How fa8_fwd_decode_splitkv computes a problem; the result is identical for every call with
+ * the same host-side values. Within one split, the keys are processed in blocks of block_keys
+ * keys (counted from key 0): one online-softmax step (row max, lazy rescale, P, PV) per block.
+ * key_groups independent online-softmax states may share a split: state k takes the blocks b
+ * with b mod key_groups == k, and the states of a row are merged by the same log-sum-exp rule
+ * as fa8_combine before the split's partial is written (the split-KV construction of "Native
+ * FP8 ... for Hopper", Design, Decode launches); the kernels here use key_groups = 1.
+ * kernel: 0 = one wave per (kv head, split, batch, 32-row block); 1 = one wave per (group of
+ * heads_per_workgroup kv heads, split, batch), whose rows fill one 16-row MFMA block. Needs no
+ * GPU. */
+typedef struct {
+  int32_t kernel;
+  int32_t block_keys;
+  int32_t key_groups;
+  int32_t heads_per_workgroup;
+  int64_t workgroups;
+} fa8_decode_plan_info;
+fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_decode_plan_info* info);
 
 /* Bytes of o_partial + lse_partial for the given problem (o_partial first, then lse_partial,
  * each 256-byte aligned), or 0 on overflow. */

@@ -72,12 +72,22 @@ def e4m3_encode_rne(x: np.ndarray, saturate: bool = True) -> np.ndarray:
 
 def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_splits: int = 1,
             l_from_rounded: bool = False, heads: Optional[list] = None, batches: Optional[list] = None,
-            stats: Optional[dict] = None):
+            stats: Optional[dict] = None, interleave: int = 1, granule: Optional[int] = None):
     """Run the method on every query row of the selected (batch, head) pairs.
+
+    Splits cut the keys into contiguous runs of granules of `granule` keys (default tile_n;
+    split s takes granules [s*G/S, (s+1)*G/S) of the G granules covering [0, Sk)). Inside a
+    split, tile t (tile_n keys, counted from key 0) goes to running state t mod `interleave`;
+    each state runs the online softmax on its own, and the states of a split are merged with
+    the log-sum-exp combine, like the splits themselves (the split-KV construction: parts of the
+    KV range rescaled independently and merged by their LSEs, "Native FP8 (E4M3 Q/K/V) forward
+    for Hopper", Design, Decode launches).
 
     Returns a dict {(b, h): (O [Sq_b, dv] float64, LSE [Sq_b] float64)}.
     stats, if given, receives 'clipped' (number of P values that exceeded 448) and 'pmax'.
     """
+    g_keys = granule if granule is not None else tile_n
+    assert g_keys % tile_n == 0 and interleave >= 1
     dec = e4m3_table()
     B, Hq, Hkv, d, dv = inp.batch, inp.heads_q, inp.heads_kv, inp.d, inp.dv
     g = Hq // Hkv
@@ -130,13 +140,18 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
             kf = dec[kb[:, kvh, :]]                      # [sk, d]
             vf = dec[vb[:, kvh, :]]                      # [sk, dv]
             ntiles = (sk + tile_n - 1) // tile_n
+            per = g_keys // tile_n
+            ngran = (sk + g_keys - 1) // g_keys
             parts_o, parts_l = [], []
-            for s in range(num_splits):
-                t0, t1 = (s * ntiles) // num_splits, ((s + 1) * ntiles) // num_splits
+            for s, k in [(s, k) for s in range(num_splits) for k in range(interleave)]:
+                t0 = ((s * ngran) // num_splits) * per
+                t1 = min((((s + 1) * ngran) // num_splits) * per, ntiles)
                 m = np.full(sq, -np.inf, np.float32)
                 l = np.zeros(sq, np.float32)
                 o = np.zeros((sq, dv), np.float32)
                 for t in range(t0, t1):
+                    if t % interleave != k:
+                        continue
                     js = np.arange(t * tile_n, min((t + 1) * tile_n, sk))
                     sc = (qf @ kf[js].T).astype(np.float32)          # exact dots, rounded to fp32
                     vis = (js[None, :] >= lo[:, None]) & (js[None, :] < hi[:, None])
@@ -164,6 +179,12 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
                     ls = np.where(l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(np.where(l > 0, l, 1.0)) - bias), -np.inf)
                 parts_o.append(on)
                 parts_l.append(ls)
+            if interleave > 1:
+                # merge the running states of each split first (a split's partial), then splits
+                merged = [combine(np.stack(parts_o[i:i + interleave]), np.stack(parts_l[i:i + interleave]))
+                          for i in range(0, len(parts_o), interleave)]
+                parts_o = [x[0] for x in merged]
+                parts_l = [x[1] for x in merged]
             if num_splits == 1:
                 out[(b, h)] = (parts_o[0], parts_l[0])
             else:

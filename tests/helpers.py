@@ -54,6 +54,13 @@ def run_prefill(inp, return_lse=True):
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
+def decode_schedule(inp, num_splits):
+    """(block_keys, key_groups) of the decode kernel the library picks (fa8_decode_plan)."""
+    q, k, v, kw = tensors(inp)
+    plan = binding.decode_plan(q, k, v, num_splits=num_splits, **kw)
+    return plan["block_keys"], plan["key_groups"]
+
+
 def run_decode(inp, num_splits=None):
     q, k, v, kw = tensors(inp)
     out, lse = binding.decode(q, k, v, num_splits=num_splits, out_dtype=out_dtype(inp), return_lse=True, **kw)
@@ -141,6 +148,7 @@ def prefill_tile(d: int, dv: int) -> int:
 
 
 def emulate_full(inp, num_splits: int = 1, with_lse: bool = False, tile_n: int = GRANULE, **kw):
+    # kw: passed to the emulator (interleave, granule, l_from_rounded, ...)
     """The oracle package's step-by-step method emulator, reshaped to the output layout (and the
     LSE to [B, Hq, Sq] / [Hq, total_q] when with_lse)."""
     from oracle import emulator
@@ -160,6 +168,8 @@ def emulate_full(inp, num_splits: int = 1, with_lse: bool = False, tile_n: int =
         for (b, h), (o, l) in res.items():
             out[b, :, h] = o
             lse[b, h] = l
+    # the method's last step: round to the output dtype (RNE), as the kernel's store does
+    out = torch.from_numpy(out).to(out_dtype(inp)).double().numpy()
     return (out, lse) if with_lse else out
 
 
@@ -211,7 +221,8 @@ def compare_to_emulator(got, emu, ref, what=""):
 LSE_METHOD = -math.log(1 - 2.0 ** -4) + 1e-4
 
 
-def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits=1, tile_n=GRANULE):
+def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits=1, tile_n=GRANULE,
+                         interleave=1, granule=None):
     """Parity of one kernel result with the oracle.
 
     strict: every element within 2e-2 + 2e-2 |ref| (the stated tolerance), except elements where
@@ -220,7 +231,9 @@ def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits
       Needs emu; their count is reported.
     not strict: every element inside the method's rounding bound (few-key rows, sharp softmax).
     LSE: within the method's bound -ln(1 - 2^-4); rows beyond 1e-2 are counted and reported.
-    emu: also the global kernel-emulator RMS check of compare_to_emulator.
+    emu: also the global kernel-emulator RMS check of compare_to_emulator; the emulator runs the
+      kernel's schedule (tile_n keys per step, `interleave` running states per split, splits cut
+      on `granule`-key granules).
     Returns a one-line summary."""
     ref, rlse = oracle.attention_full(inp)
     got = np.asarray(got, np.float64)
@@ -230,7 +243,8 @@ def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits
     bound = method_bound(inp, ref)
     emu_o = emu_l = None
     if emu:
-        emu_o, emu_l = emulate_full(inp, num_splits=num_splits, with_lse=True, tile_n=tile_n)
+        emu_o, emu_l = emulate_full(inp, num_splits=num_splits, with_lse=True, tile_n=tile_n, interleave=interleave,
+                                    granule=granule)
     n_method = 0
     if strict:
         bad = err > ATOL + RTOL * np.abs(ref)

@@ -53,6 +53,14 @@ def test_struct_layout_matches_c():
     assert ctypes.sizeof(binding.FwdParams) == size
     assert binding.FwdParams.lse_row_stride.offset == off_last
     assert binding.FwdParams.softmax_scale.offset == off_scale
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "fa8.h"\nint main(void){printf("%zu %zu",'
+           ' sizeof(fa8_decode_plan_info), offsetof(fa8_decode_plan_info, workgroups));return 0;}\n')
+    r = subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-x", "c", "-", "-o", exe], input=src,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    size, off_wg = map(int, subprocess.run([exe], capture_output=True, text=True).stdout.split())
+    assert ctypes.sizeof(binding.DecodePlan) == size
+    assert binding.DecodePlan.workgroups.offset == off_wg
 
 
 def _cpu(shape, dtype=torch.uint8):
@@ -158,3 +166,44 @@ def test_num_splits_heuristic_bounds():
     # long single-sequence decode gets many splits; a full batch gets few
     assert binding.decode_num_splits(4, 1, 131072) >= 64
     assert binding.decode_num_splits(512, 8, 8192) <= 2
+
+
+def _paged_decode_args(b=64, hq=32, hkv=8, d=128, page=16, max_sk=8192):
+    # host-side values only (nothing is read on the device): a few pages suffice
+    q = _cpu((b, hq, d))
+    k = _cpu((4, page, hkv, d))
+    v = _cpu((4, page, hkv, d))
+    kw = dict(cu_seqlens_q=torch.arange(b + 1, dtype=torch.int32), seqused_k=torch.full((b,), 100, dtype=torch.int32),
+              block_table=torch.zeros((b, max_sk // page), dtype=torch.int32), max_seqlen_q=1, max_seqlen_k=max_sk)
+    return q, k, v, kw
+
+
+def test_num_splits_for_picks_per_kernel(monkeypatch):
+    # paged GQA decode shape: the several-heads kernel has 64 x 2 one-wave units per split, so
+    # 4 x 256 CUs / 128 = 8 splits; the per-head kernel has 64 x 8 units, 16 x 256 / 512 = 8
+    q, k, v, kw = _paged_decode_args()
+    assert binding.decode_num_splits_for(q, k, v, **kw) == 8
+    monkeypatch.setenv("FA8_DECODE_KERNEL", "lanes")
+    assert binding.decode_num_splits_for(q, k, v, **kw) == 8
+    monkeypatch.delenv("FA8_DECODE_KERNEL")
+    # long single-kv-head decode: capped at FA8_MAX_SPLITS, at least 4 granules per split
+    q, k, v, kw = _paged_decode_args(b=4, hq=8, hkv=1, page=64, max_sk=131072)
+    n = binding.decode_num_splits_for(q, k, v, **kw)
+    assert 64 <= n <= binding.MAX_SPLITS
+    # short sequences: at least four 64-key granules per split
+    q, k, v, kw = _paged_decode_args(b=1, max_sk=512)
+    assert binding.decode_num_splits_for(q, k, v, **kw) == 2
+
+
+def test_decode_plan(monkeypatch):
+    q, k, v, kw = _paged_decode_args()
+    plan = binding.decode_plan(q, k, v, num_splits=16, **kw)
+    # paged GQA decode (4 rows per kv head): 4 kv heads per wave fill its 16 MFMA rows, 16-key
+    # steps, 64 batches x 2 head groups x 16 splits
+    assert plan == dict(kernel=1, block_keys=16, key_groups=1, heads_per_workgroup=4, workgroups=64 * 2 * 16)
+    monkeypatch.setenv("FA8_DECODE_KERNEL", "lanes")
+    plan = binding.decode_plan(q, k, v, num_splits=16, **kw)
+    assert plan == dict(kernel=0, block_keys=64, key_groups=1, heads_per_workgroup=1, workgroups=64 * 8 * 16)
+    monkeypatch.delenv("FA8_DECODE_KERNEL")
+    with pytest.raises(binding.FA8Error):
+        binding.decode_plan(q, k, v, num_splits=0, **kw)

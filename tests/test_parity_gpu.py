@@ -10,8 +10,8 @@ import oracle
 from fa8_fwd_amd import binding
 from fa8_fwd_amd import inputs as gen
 
-from helpers import (GRANULE, check_against_oracle, compare, compare_lse, prefill_tile, run_decode, run_prefill,
-                     split_key_ranges, tensors)
+from helpers import (GRANULE, check_against_oracle, compare, compare_lse, decode_schedule, prefill_tile, run_decode,
+                     run_prefill, split_key_ranges, tensors)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,17 +121,35 @@ def test_descale_modes(mode):
 
 def _decode_check(inp, num_splits, what, strict=True, emu=True):
     got, glse = run_decode(inp, num_splits)
-    # the emulator splits the same 64-key granules as the kernel when the rows see [0, Sk)
+    # the emulator splits the same 64-key granules as the kernel when the rows see [0, Sk), and
+    # follows the kernel's blocking (fa8_decode_plan)
+    use_emu = emu and num_splits is not None and inp.window_left < 0
     ns = 1 if (num_splits is None or inp.window_left >= 0) else num_splits
-    _check(inp, got, glse, what, strict, emu and num_splits is not None and inp.window_left < 0, ns)
+    tile_n, inter = decode_schedule(inp, ns) if use_emu else (GRANULE, 1)
+    print(check_against_oracle(inp, got, glse, what, strict, use_emu, ns, tile_n, interleave=inter, granule=GRANULE),
+          flush=True)
     return got
 
 
+@pytest.mark.parametrize("kernel", ["rows", "lanes"])
 @pytest.mark.parametrize("num_splits", [1, 3, None])
-def test_decode_paged_gqa(num_splits):
-    # the paged GQA decode workload at batch 8: lengths 1k-4k, per-(b, kv_head) descales
+def test_decode_paged_gqa(num_splits, kernel, monkeypatch):
+    # the paged GQA decode workload at batch 8: lengths 1k-4k, per-(b, kv_head) descales; both
+    # decode kernels (whole-row and per-head)
+    if kernel == "lanes":
+        monkeypatch.setenv("FA8_DECODE_KERNEL", "lanes")
     inp = gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096)
-    _decode_check(inp, num_splits, f"paged decode b8 splits={num_splits}")
+    _decode_check(inp, num_splits, f"paged decode b8 splits={num_splits} {kernel}")
+
+
+@pytest.mark.parametrize("layout", ["dense", "varlen"])
+def test_decode_contiguous_kv(layout):
+    # split-KV decode on contiguous K/V (fixed-length BSHD and packed varlen)
+    if layout == "dense":
+        inp = gen.make_dense(40, 3, 1, 777, 8, 2, 128, 128, descales=(("uniform", 0.5, 2.0),) * 3)
+    else:
+        inp = gen.make_varlen(41, [1, 1, 1, 1], [300, 64, 1, 2000], 8, 2, 128, 128)
+    _decode_check(inp, 3, f"decode contiguous {layout}")
 
 
 def test_decode_short_sequences_peaked():
