@@ -98,8 +98,8 @@ fa8_status validate(const fa8_fwd_params* p, int32_t num_splits) {
     if (!aligned(p->block_table, 4)) return fail(FA8_ERR_INVALID, "block_table must be 4-byte aligned");
   }
   {
-    // row offsets inside one page (paged) or one 64-key tile (contiguous) are 32-bit
-    const int64_t rows = p->block_table ? (int64_t)p->page_size : 64;
+    // row offsets inside one page (paged) or one KV tile of up to 128 keys (contiguous) are 32-bit
+    const int64_t rows = p->block_table ? (int64_t)p->page_size : 128;
     const int64_t rs = p->k_row_stride > p->v_row_stride ? p->k_row_stride : p->v_row_stride;
     if (rows * rs + 256 >= ((int64_t)1 << 31))
       return fail(FA8_ERR_INVALID, "K/V row stride %lld too large for %lld rows", (long long)rs, (long long)rows);

@@ -111,6 +111,44 @@ __device__ __forceinline__ v4i ld_buffer16_nt(const uint8_t* base, int nrec, uin
       __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, __builtin_amdgcn_readfirstlane(nrec), 0x00020000);
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 2));
 }
+// 16 bytes per lane global -> LDS (M0 = wave-uniform LDS destination, lane L writes LDS bytes
+// [dst + 16 L, +16)), from a uniform base plus this lane's 32-bit offset (saddr form) or from a
+// per-lane address (vaddr form). Issued as inline assembly on purpose: the compiler's wait-count
+// pass cannot tell which LDS bytes such a copy writes, so with the builtin every later LDS read
+// would wait for all outstanding copies, serializing the next tile's copy with this tile's math.
+// Callers order the copies with explicit wait_vmcnt + barriers. The s_nop covers the
+// SGPR-write-to-VMEM and M0 hazards of operands produced just before the statement.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* base, uint32_t voff, uint32_t lds_dst) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t ua = ((uint64_t)hi << 32) | lo;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(ua), "s"(m0)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void copy16_to_lds_vaddr(const uint8_t* src, uint32_t lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(m0)
+      : "memory", "m0");
+}
+// max of three floats as one v_max3_f32 (fmaxf would first quiet each MFMA result with an extra
+// v_max_f32 x, x, which IEEE mode requires of maxnum)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 // Cross-lane moves within a wave through the gfx950 permlane swaps (VALU, no LDS round trip).
 // permlane16_swap(x, x) leaves {x of row 2k, x of row 2k+1} in both rows of each pair of
 // 16-lane rows, permlane32_swap(x, x) leaves {x of rows 0-1, x of rows 2-3} in both halves.
@@ -294,8 +332,8 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
 #pragma unroll
   for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 0; r < 16; r += 2) mx = max3f(mx, sacc[kb][r], sacc[kb][r + 1]);
+  mx = max_xor32(mx);
   const float mt = mx * c;
   float alpha = 1.0f;
   if (mt - m_run > kTau) {          // also true when m_run = -inf and mt is finite
@@ -304,9 +342,8 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
   const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
 
-  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order; row sum of the rounded P ----
+  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order ----
   v8i pop[PK];
-  float lsum = 0.0f;
 #pragma unroll
   for (int pk = 0; pk < PK; pk++)
 #pragma unroll
@@ -319,11 +356,18 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pop[pk][w] = word;
-      const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
-      const auto r23 = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-      lsum += (r01[0] + r01[1]) + (r23[0] + r23[1]);
     }
-  l_run = alpha * l_run + lsum;
+  // ---- row sum of the rounded P on the MFMA: an all-ones A operand (E4M3 1.0 = 0x38) makes
+  //      every output row the sum over the keys of this lane's query row ----
+  {
+    const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+    v16f rs;
+#pragma unroll
+    for (int r = 0; r < 16; r++) rs[r] = 0.0f;
+#pragma unroll
+    for (int pk = 0; pk < PK; pk++) rs = mfma_32x32x64_fp8(ones, pop[pk], rs);
+    l_run = alpha * l_run + rs[0];
+  }
 
   // ---- O_tile = V^T P^T from zero over this tile, then O = alpha * O + O_tile ----
   const int trj = (lane & 15) >> 1;
@@ -575,14 +619,22 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     FA8_LDS uint8_t* kt = (FA8_LDS uint8_t*)smem + st * STAGE;
     FA8_LDS uint8_t* vt = kt + KTILE;
     const int j0 = t * BN;
+    const bool paged = ka.trow != nullptr;
+    // contiguous K/V: the tile's first row is a uniform base, rows are 32-bit offsets from it
+    // (at most BN rows x row stride < 2^31 bytes, checked on the host)
+    const uint8_t* kb0 = p.k + ka.kbase + (int64_t)j0 * ka.k_rs;
+    const uint8_t* vb0 = p.v + ka.vbase + (int64_t)j0 * ka.v_rs;
 #pragma unroll
     for (int i = 0; i < KINST; i++) {
       const int blk = wave * KINST + i;
       const int pos = blk * 1024 + lane * 16;
       const int row = pos / D, pc = (pos - row * D) >> 4;
       const int j = min(j0 + row, si.sk - 1);
-      const uint8_t* src = p.k + ka.k(j) + swz<KCH>(pc, k_sv(row)) * 16;
-      __builtin_amdgcn_global_load_lds(src, (FA8_LDS void*)(kt + blk * 1024), 16, 0, 0);
+      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(kt + blk * 1024);
+      if (paged)
+        copy16_to_lds_vaddr(p.k + ka.k(j) + swz<KCH>(pc, k_sv(row)) * 16, dst);
+      else
+        copy16_to_lds(kb0, (uint32_t)((j - j0) * (int)ka.k_rs + swz<KCH>(pc, k_sv(row)) * 16), dst);
     }
 #pragma unroll
     for (int i = 0; i < VINST; i++) {
@@ -590,8 +642,11 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
       const int pos = blk * 1024 + lane * 16;
       const int row = pos / DV, pc = (pos - row * DV) >> 4;
       const int j = min(j0 + row, si.sk - 1);
-      const uint8_t* src = p.v + ka.v(j) + swz<VCH>(pc, v_sv(row)) * 16;
-      __builtin_amdgcn_global_load_lds(src, (FA8_LDS void*)(vt + blk * 1024), 16, 0, 0);
+      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(vt + blk * 1024);
+      if (paged)
+        copy16_to_lds_vaddr(p.v + ka.v(j) + swz<VCH>(pc, v_sv(row)) * 16, dst);
+      else
+        copy16_to_lds(vb0, (uint32_t)((j - j0) * (int)ka.v_rs + swz<VCH>(pc, v_sv(row)) * 16), dst);
     }
   };
 
@@ -618,7 +673,7 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     __syncthreads();   // ... and every other wave's; all reads of stage st are done
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run;   // the MFMA row sums already cover both lanes of a row
   if (!valid) return;
   store_row<DV, false>(p, oacc, m_run, l_tot, dvs, hgrp, b, si.q0, qi, qh, 0);
 }
