@@ -89,7 +89,14 @@ __device__ __forceinline__ int swz(int ch, int sv) {
   if ((ch | 1) < NCH) return ch ^ (sv & 1);
   return ch;
 }
-__device__ __forceinline__ int k_sv(int row) { return row & 7; }
+// K rows are read 16 consecutive rows at a time (one 16-byte chunk each) by ds_read_b128; the LDS
+// serves 256 bytes per cycle from 64 banks, so rows that share a 256-byte window (2 rows of
+// 128 bytes, 4 of 64) need different chunk positions: the swizzle key is the window index of
+// the row, which gives 16 distinct (window offset, chunk) pairs for 16 rows.
+template <int D>
+__device__ __forceinline__ int k_sv(int row) {
+  return D == 64 ? (row >> 2) : (D == 128 ? (row >> 1) : row);
+}
 // V is read 8 rows at a time by ds_read_b64_tr_b8 with row sets {0-3, 8-11} + 4h (+16r):
 // bits 0, 1 and 3 of the row make those 8 rows land in 8 different chunks.
 __device__ __forceinline__ int v_sv(int row) { return (row & 3) | ((row >> 1) & 4); }
@@ -308,8 +315,8 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
       if (off < D) {
         const int ch = off >> 4;
-        const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch, k_sv(row)) * 16);
-        const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch + 1, k_sv(row)) * 16);
+        const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch, k_sv<D>(row)) * 16);
+        const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch + 1, k_sv<D>(row)) * 16);
         kop = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
       }
       sacc[kb] = mfma_32x32x64_fp8(kop, qop[ks], sacc[kb]);
@@ -427,8 +434,8 @@ __device__ __forceinline__ void attn_tile16(const FA8_LDS uint8_t* kt, const FA8
       v8i kop = {0, 0, 0, 0, 0, 0, 0, 0};
       if (off < D) {
         const int ch = off >> 4;
-        const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch, k_sv(row)) * 16);
-        const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch + 1, k_sv(row)) * 16);
+        const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch, k_sv<D>(row)) * 16);
+        const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(ch + 1, k_sv<D>(row)) * 16);
         kop = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
       }
 #pragma unroll
@@ -632,9 +639,9 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
       const int j = min(j0 + row, si.sk - 1);
       const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(kt + blk * 1024);
       if (paged)
-        copy16_to_lds_vaddr(p.k + ka.k(j) + swz<KCH>(pc, k_sv(row)) * 16, dst);
+        copy16_to_lds_vaddr(p.k + ka.k(j) + swz<KCH>(pc, k_sv<D>(row)) * 16, dst);
       else
-        copy16_to_lds(kb0, (uint32_t)((j - j0) * (int)ka.k_rs + swz<KCH>(pc, k_sv(row)) * 16), dst);
+        copy16_to_lds(kb0, (uint32_t)((j - j0) * (int)ka.k_rs + swz<KCH>(pc, k_sv<D>(row)) * 16), dst);
     }
 #pragma unroll
     for (int i = 0; i < VINST; i++) {
@@ -880,7 +887,7 @@ fa8_decode_kernel(const KParams p) {
     for (int u = 0; u < KPT; u++) {
       const int cid = u * 64 + lane;
       const int row = cid / KCH, ch = cid - row * KCH;
-      *reinterpret_cast<v4i*>(smem + row * D + swz<KCH>(ch, k_sv(row)) * 16) = ks[u];
+      *reinterpret_cast<v4i*>(smem + row * D + swz<KCH>(ch, k_sv<D>(row)) * 16) = ks[u];
     }
 #pragma unroll
     for (int u = 0; u < VPT; u++) {
