@@ -12,10 +12,12 @@ duration is measured with HIP events on its launch stream over the timed region.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
 import platform
+import re
 import sys
 import time
 
@@ -79,6 +81,50 @@ def decode_step_bytes(inp) -> int:
 
 
 # ---------------------------------------------------------------------------------------------
+# HBM traffic from hardware counters (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE), recorded in a
+# committed summary under profiles/ together with the hash of the kernel sources it was taken on
+# ---------------------------------------------------------------------------------------------
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's device and host sources (what decides the launched kernels)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fa8_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(summary: str):
+    """HBM bytes per launch recorded in profiles/<summary>, or None when there is no record or
+    the sources have changed since the counters were taken."""
+    try:
+        with open(os.path.join(ROOT, "profiles", summary)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    sha = re.search(r"kernel source sha256: `([0-9a-f]{64})`", text)
+    nbytes = re.search(r"traffic per launch: ([0-9]+) bytes", text)
+    if not (sha and nbytes) or sha.group(1) != kernel_source_hash():
+        return None
+    return int(nbytes.group(1))
+
+
+def copy_calibration(mib: int, dev) -> None:
+    """A plain copy-like kernel of known traffic (reads and writes `mib` MiB once each), run three
+    times so that a counter pass over this program can scale FETCH_SIZE / WRITE_SIZE."""
+    n = mib * 2**20 // 4
+    src = torch.arange(n, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+# ---------------------------------------------------------------------------------------------
 
 def to_dev(x, dev):
     if x is None:
@@ -124,6 +170,18 @@ def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None):
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     return (t1 - t0) * 1e3 / steps, kernel_ms, S
+
+
+def decode_kernel_name(inp, dev, num_splits: int) -> str:
+    """Name of the decode kernel the library's plan picks for this workload."""
+    q, k, v, kw = device_args(inp, dev)
+    plan = binding.decode_plan(q, k, v, num_splits=num_splits, **kw)
+    paged = inp.block_table is not None
+    if plan["kernel"] == 1:
+        step_page = (not paged) or inp.page_size >= plan["block_keys"]
+        return (f"fa8_decode_heads_kernel<{inp.d},{inp.dv},{plan['heads_per_workgroup']},{int(paged)},{int(step_page)}>"
+                f" (split-KV decode, {plan['heads_per_workgroup']} kv heads per wave, {plan['workgroups']} waves)")
+    return f"fa8_decode_kernel<{inp.d},{inp.dv},...> (split-KV decode, one kv head per wave, {plan['workgroups']} waves)"
 
 
 def bench_prefill(inp, steps: int, warmup: int, dev):
@@ -229,6 +287,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time per workload")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a copy kernel of MIB MiB (for scaling counter passes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -240,6 +300,8 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     binding.load()
+    if args.calibrate_copy > 0:
+        copy_calibration(args.calibrate_copy, dev)
 
     dec = gen.paged_gqa_decode(1)
     ms_step, kern_ms, S = bench_decode(dec, args.steps, args.warmup, dev, args.num_splits or None)
@@ -264,9 +326,10 @@ def main():
                    "d": dec.d, "page_size": dec.page_size, "seqlens_k": "uniform [1024, 8192], seed 1",
                    "sum_seqlen_k": int(dec.seqlens_k().sum()), "num_splits": S, "out": "bf16",
                    "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": "fa8_decode_rows_kernel<128,128,4,2> (split-KV decode, paged, whole rows)",
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(dec, dev, S),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"fa8_decode_heads_kernel_{dec.name}_traffic.md"),
                      "kernel_ms": round(kern_ms, 5), "bytes_per_launch": kbytes},
     }
     if not args.no_prefill:
@@ -280,7 +343,9 @@ def main():
             "steps": args.prefill_steps, "flop_per_step": flop, "pct_of_fp8_peak": round(100 * tfl / FP8_PEAK_TFLOPS, 2),
             "roofline": {"bound": "mfma", "kernel": "fa8_prefill_kernel<128,128,128> (prefill)",
                          "achieved": round(ktfl, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ktfl / FP8_PEAK_TFLOPS, 4), "traffic": None, "kernel_ms": round(p_kern, 4)},
+                         "frac": round(ktfl / FP8_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic(f"fa8_prefill_kernel_{pre.name}_traffic.md"),
+                         "kernel_ms": round(p_kern, 4)},
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
