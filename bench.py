@@ -281,8 +281,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=50)
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -334,7 +335,7 @@ def main():
     }
     if not args.no_prefill:
         pre = gen.causal_prefill(2)
-        p_ms, p_kern = bench_prefill(pre, args.prefill_steps, max(2, args.warmup // 5), dev)
+        p_ms, p_kern = bench_prefill(pre, args.prefill_steps, args.prefill_warmup, dev)
         flop = prefill_flop(pre)
         tfl = flop / (p_ms * 1e-3) / 1e12
         ktfl = flop / (p_kern * 1e-3) / 1e12

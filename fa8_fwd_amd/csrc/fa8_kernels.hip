@@ -149,6 +149,27 @@ __device__ __forceinline__ void copy16_to_lds_vaddr(const uint8_t* src, uint32_t
       : "v"(src), "s"(m0)
       : "memory", "m0");
 }
+// 16 bytes per lane buffer -> LDS: lane L's bytes at offset voff of the buffer described by the
+// wave-uniform descriptor rsrc land at LDS [lds_dst + 16 L, +16); offsets at or past the
+// descriptor's range read as zeros without a memory access. Inline assembly for the same reason
+// as copy16_to_lds.
+__device__ __forceinline__ void buffer_copy16_to_lds(v4i rsrc, uint32_t voff, uint32_t lds_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_dst);
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(m0)
+      : "memory", "m0");
+}
+// Descriptor of nrec bytes from a wave-uniform base (no stride, raw buffer).
+__device__ __forceinline__ v4i buffer_rsrc(const uint8_t* base, uint32_t nrec) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (v4i){(int)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (int)(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffff),
+               (int)__builtin_amdgcn_readfirstlane(nrec), 0x00020000};
+}
 // max of three floats as one v_max3_f32 (fmaxf would first quiet each MFMA result with an extra
 // v_max_f32 x, x, which IEEE mode requires of maxnum)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -559,7 +580,7 @@ __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[D
 // Workgroups are numbered so that each XCD (workgroup id mod 8) receives a contiguous run of
 // the work list, ordered by (batch, kv head), so the workgroups that share K/V share an L2.
 // ------------------------------------------------------------------------------------------
-template <int D, int DV, int BN>
+template <int D, int DV, int BN, bool PAGED>
 __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   constexpr int NW = 4, BM = NW * 32;
   constexpr int KTILE = BN * D, VTILE = BN * DV, STAGE = KTILE + VTILE;
@@ -570,7 +591,8 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps LDS tile addresses scalar
   const int hgrp = lane >> 5, lrow = lane & 31;
 
   // ---- XCD-aware work index ----
@@ -621,39 +643,57 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   // Direct global->LDS loads of tile t into stage st. Load instruction i of this wave fills
   // LDS bytes [1024*(wave*KINST + i), +1024) of the K tile, lane L its 16 bytes at 16*L: that
   // position is physical chunk pc of row r, which holds logical chunk swz(pc) (an involution).
-  // Rows past the sequence read its last valid row (masked to P = 0; finite V keeps 0*V = 0).
+  // Contiguous K/V: a buffer descriptor per tile whose range ends at the sequence's last row, and
+  // per-lane offsets fixed for the whole loop; rows past the sequence read as zeros (masked to
+  // P = 0, and 0 * V = 0). Paged K/V: per-lane addresses through the block table; rows past the
+  // sequence read its last valid row.
+  uint32_t k_off[KINST], v_off[VINST];
+#pragma unroll
+  for (int i = 0; i < KINST; i++) {
+    const int pos = (wave * KINST + i) * 1024 + lane * 16;
+    const int row = pos / D, pc = (pos - row * D) >> 4;
+    k_off[i] = (uint32_t)(row * (int)ka.k_rs + swz<KCH>(pc, k_sv<D>(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VINST; i++) {
+    const int pos = (wave * VINST + i) * 1024 + lane * 16;
+    const int row = pos / DV, pc = (pos - row * DV) >> 4;
+    v_off[i] = (uint32_t)(row * (int)ka.v_rs + swz<VCH>(pc, v_sv(row)) * 16);
+  }
   auto dma_tile = [&](int t, int st) {
     FA8_LDS uint8_t* kt = (FA8_LDS uint8_t*)smem + st * STAGE;
     FA8_LDS uint8_t* vt = kt + KTILE;
     const int j0 = t * BN;
-    const bool paged = ka.trow != nullptr;
-    // contiguous K/V: the tile's first row is a uniform base, rows are 32-bit offsets from it
-    // (at most BN rows x row stride < 2^31 bytes, checked on the host)
-    const uint8_t* kb0 = p.k + ka.kbase + (int64_t)j0 * ka.k_rs;
-    const uint8_t* vb0 = p.v + ka.vbase + (int64_t)j0 * ka.v_rs;
+    if constexpr (!PAGED) {
+      // valid rows of the tile: at most BN rows x row stride < 2^31 bytes (checked on the host)
+      const int rows = min(si.sk - j0, BN);
+      const v4i kr = buffer_rsrc(p.k + ka.kbase + (int64_t)j0 * ka.k_rs, (uint32_t)((rows - 1) * (int)ka.k_rs + D));
+      const v4i vr = buffer_rsrc(p.v + ka.vbase + (int64_t)j0 * ka.v_rs, (uint32_t)((rows - 1) * (int)ka.v_rs + DV));
 #pragma unroll
-    for (int i = 0; i < KINST; i++) {
-      const int blk = wave * KINST + i;
-      const int pos = blk * 1024 + lane * 16;
-      const int row = pos / D, pc = (pos - row * D) >> 4;
-      const int j = min(j0 + row, si.sk - 1);
-      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(kt + blk * 1024);
-      if (paged)
-        copy16_to_lds_vaddr(p.k + ka.k(j) + swz<KCH>(pc, k_sv<D>(row)) * 16, dst);
-      else
-        copy16_to_lds(kb0, (uint32_t)((j - j0) * (int)ka.k_rs + swz<KCH>(pc, k_sv<D>(row)) * 16), dst);
-    }
+      for (int i = 0; i < KINST; i++)
+        buffer_copy16_to_lds(kr, k_off[i], (uint32_t)reinterpret_cast<uintptr_t>(kt + (wave * KINST + i) * 1024));
 #pragma unroll
-    for (int i = 0; i < VINST; i++) {
-      const int blk = wave * VINST + i;
-      const int pos = blk * 1024 + lane * 16;
-      const int row = pos / DV, pc = (pos - row * DV) >> 4;
-      const int j = min(j0 + row, si.sk - 1);
-      const uint32_t dst = (uint32_t)reinterpret_cast<uintptr_t>(vt + blk * 1024);
-      if (paged)
-        copy16_to_lds_vaddr(p.v + ka.v(j) + swz<VCH>(pc, v_sv(row)) * 16, dst);
-      else
-        copy16_to_lds(vb0, (uint32_t)((j - j0) * (int)ka.v_rs + swz<VCH>(pc, v_sv(row)) * 16), dst);
+      for (int i = 0; i < VINST; i++)
+        buffer_copy16_to_lds(vr, v_off[i], (uint32_t)reinterpret_cast<uintptr_t>(vt + (wave * VINST + i) * 1024));
+    } else {
+#pragma unroll
+      for (int i = 0; i < KINST; i++) {
+        const int blk = wave * KINST + i;
+        const int pos = blk * 1024 + lane * 16;
+        const int row = pos / D, pc = (pos - row * D) >> 4;
+        const int j = min(j0 + row, si.sk - 1);
+        copy16_to_lds_vaddr(p.k + ka.k(j) + swz<KCH>(pc, k_sv<D>(row)) * 16,
+                            (uint32_t)reinterpret_cast<uintptr_t>(kt + blk * 1024));
+      }
+#pragma unroll
+      for (int i = 0; i < VINST; i++) {
+        const int blk = wave * VINST + i;
+        const int pos = blk * 1024 + lane * 16;
+        const int row = pos / DV, pc = (pos - row * DV) >> 4;
+        const int j = min(j0 + row, si.sk - 1);
+        copy16_to_lds_vaddr(p.v + ka.v(j) + swz<VCH>(pc, v_sv(row)) * 16,
+                            (uint32_t)reinterpret_cast<uintptr_t>(vt + blk * 1024));
+      }
     }
   };
 
@@ -1418,8 +1458,12 @@ constexpr int prefill_tile() { return (D + DV) <= 256 ? 128 : 64; }
 template <int D, int DV>
 static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
   const int64_t nwork = (int64_t)kp.nmb * kp.hq * kp.batch;
-  hipLaunchKernelGGL((fa8_prefill_kernel<D, DV, prefill_tile<D, DV>()>), dim3((unsigned)nwork), dim3(256), 0,
-                     stream, kp);
+  if (kp.page_shift >= 0)
+    hipLaunchKernelGGL((fa8_prefill_kernel<D, DV, prefill_tile<D, DV>(), true>), dim3((unsigned)nwork), dim3(256), 0,
+                       stream, kp);
+  else
+    hipLaunchKernelGGL((fa8_prefill_kernel<D, DV, prefill_tile<D, DV>(), false>), dim3((unsigned)nwork), dim3(256), 0,
+                       stream, kp);
   return hipGetLastError();
 }
 template <int D, int DV, int NQB>
