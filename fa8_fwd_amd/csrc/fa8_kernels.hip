@@ -170,6 +170,14 @@ __device__ __forceinline__ v4i buffer_rsrc(const uint8_t* base, uint32_t nrec) {
                (int)(__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffff),
                (int)__builtin_amdgcn_readfirstlane(nrec), 0x00020000};
 }
+// E4M3 (RNE) of a and b into bytes 0 and 1 of the result; bytes 2 and 3 are left unspecified
+// (the caller fills them with the high-half conversion). As inline assembly so that the
+// destination is not first cleared for the half the instruction keeps.
+__device__ __forceinline__ int cvt_pk_fp8_lo(float a, float b) {
+  int r;
+  __asm__("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 // max of three floats as one v_max3_f32 (fmaxf would first quiet each MFMA result with an extra
 // v_max_f32 x, x, which IEEE mode requires of maxnum)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -344,14 +352,17 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
     }
   }
 
-  // ---- mask (only tiles that cross some row's key bounds) ----
+  // ---- mask (only tiles that cross some row's key bounds): key j is visible iff
+  //      my_lo <= j < my_hi, one unsigned compare (an empty row has span 0) ----
   if (need_mask) {
+    const uint32_t span = (uint32_t)max(my_hi - my_lo, 0);
+    const int base = j0 + 4 * hgrp - my_lo;
 #pragma unroll
     for (int kb = 0; kb < KB; kb++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hgrp + (r & 3);
-        if (j < my_lo || j >= my_hi) sacc[kb][r] = kNegInf;
+        const uint32_t rel = (uint32_t)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+        if (rel >= span) sacc[kb][r] = kNegInf;
       }
   }
 
@@ -381,7 +392,7 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 1], c, nb));
       const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 2], c, nb));
       const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nb));
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      int word = cvt_pk_fp8_lo(p0, p1);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pop[pk][w] = word;
     }
@@ -497,7 +508,7 @@ __device__ __forceinline__ void attn_tile16(const FA8_LDS uint8_t* kt, const FA8
       const float p1 = fast_exp2(__builtin_fmaf(sacc[qb][w][1], c, nb));
       const float p2 = fast_exp2(__builtin_fmaf(sacc[qb][w][2], c, nb));
       const float p3 = fast_exp2(__builtin_fmaf(sacc[qb][w][3], c, nb));
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      int word = cvt_pk_fp8_lo(p0, p1);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pop[qb][w] = word;
       pop[qb][w + 4] = 0;
@@ -1303,7 +1314,7 @@ fa8_decode_heads_kernel(const KParams p) {
       const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][1], c, nb));
       const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][2], c, nb));
       const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][3], c, nb));
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      int word = cvt_pk_fp8_lo(p0, p1);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pw[kb] = word;
       const auto r01 = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
