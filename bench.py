@@ -186,7 +186,8 @@ def decode_kernel_name(inp, dev, num_splits: int) -> str:
 
 def bench_prefill(inp, steps: int, warmup: int, dev):
     q, k, v, kw = device_args(inp, dev)
-    out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=torch.bfloat16, device=dev)
+    odt = torch.float16 if inp.out_dtype == "fp16" else torch.bfloat16
+    out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=odt, device=dev)
     for _ in range(warmup):
         binding.prefill(q, k, v, out=out, **kw)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -201,6 +202,30 @@ def bench_prefill(inp, steps: int, warmup: int, dev):
     kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     assert torch.isfinite(out.float()).all(), "non-finite prefill output"
     return (t1 - t0) * 1e3 / steps, kernel_ms
+
+
+def other_workloads(args, dev) -> dict:
+    """Figures of the remaining measured workloads, reported beside the headline (not part of
+    `value`): long-KV decode (4 sequences of 131072 keys, 8/1 heads, 64-token pages; GB/s of the
+    decode step and of its kernel) and the mixed-shape varlen prefill (8 sequences, window 1024,
+    fp16 out; TFLOP/s of the visible pairs) for (d, dv) = (256, 256) and (192, 128)."""
+    out = {}
+    lk = gen.long_kv_decode(3)
+    ms, kms, S = bench_decode(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev)
+    kb = decode_kernel_bytes(lk)
+    out["long_kv_decode"] = {"workload": lk.name, "num_splits": S, "unit": "GB/s",
+                             "step_value": round(decode_step_bytes(lk) / (ms * 1e-3) / 1e9, 2),
+                             "kernel_value": round(kb / (kms * 1e-3) / 1e9, 2), "kernel_ms": round(kms, 5),
+                             "kernel_pct_of_hbm_peak": round(100 * kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    for d, dv in ((256, 256), (192, 128)):
+        mv = gen.mixed_varlen(4, d=d, dv=dv)
+        ms, kms = bench_prefill(mv, max(5, args.prefill_steps // 2), max(5, args.prefill_warmup // 5), dev)
+        fl = prefill_flop(mv)
+        out[f"mixed_varlen_d{d}x{dv}"] = {"workload": mv.name, "unit": "TFLOP/s",
+                                          "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
+                                          "kernel_pct_of_fp8_peak": round(100 * fl / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2),
+                                          "flop": fl}
+    return out
 
 
 def cpu_model() -> str:
@@ -287,6 +312,7 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's heuristic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-KV decode and mixed varlen figures")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time per workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a copy kernel of MIB MiB (for scaling counter passes)")
@@ -342,12 +368,14 @@ def main():
         line["prefill"] = {
             "workload": pre.name, "value": round(tfl, 2), "unit": "TFLOP/s", "ms_per_step": round(p_ms, 4),
             "steps": args.prefill_steps, "flop_per_step": flop, "pct_of_fp8_peak": round(100 * tfl / FP8_PEAK_TFLOPS, 2),
-            "roofline": {"bound": "mfma", "kernel": "fa8_prefill_kernel<128,128,128> (prefill)",
+            "roofline": {"bound": "mfma", "kernel": "fa8_prefill_kernel<128,128,128,false> (prefill, contiguous K/V)",
                          "achieved": round(ktfl, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ktfl / FP8_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic(f"fa8_prefill_kernel_{pre.name}_traffic.md"),
                          "kernel_ms": round(p_kern, 4)},
         }
+    if not args.no_extra:
+        line["other_workloads"] = other_workloads(args, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
         if "prefill" in line:

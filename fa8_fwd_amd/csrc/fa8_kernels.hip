@@ -1462,6 +1462,87 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   }
 }
 
+// Combine for many splits: one workgroup per output row, SP split lanes x CGP column groups
+// (CGP = dv / 4 rounded up to a power of two). Split lane sp takes splits sp, sp + SP, ...; the
+// lanes' maxima, weight sums and weighted partial rows meet in LDS. With S = 256 and dv = 128
+// each thread loads 8 splits, all issued together, instead of one row's thread walking 256.
+template <int CGP>
+__global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c) {
+  constexpr int SP = 1024 / CGP;
+  constexpr int SB = 8;
+  __shared__ float s_mx[SP], s_den[SP];
+  __shared__ v4f s_acc[SP][CGP];
+  const int tid = threadIdx.x;
+  const int q = tid % CGP, sp = tid / CGP;
+  const int tpr = c.dv / 4;
+  const int64_t rows = (int64_t)c.batch * c.max_sq * c.hq;
+  const int64_t row = blockIdx.x;
+  const int h = (int)(row % c.hq);
+  const int i = (int)((row / c.hq) % c.max_sq);
+  const int b = (int)(row / ((int64_t)c.hq * c.max_sq));
+  const int q0 = c.cu_q ? c.cu_q[b] : 0;
+  const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
+  if (i >= sq) return;   // uniform over the workgroup
+  float mx = kNegInf;
+  for (int s0 = sp; s0 < c.nsplit; s0 += SB * SP) {
+    float ls[SB];
+#pragma unroll
+    for (int k = 0; k < SB; k++) {
+      const int sidx = s0 + k * SP;
+      ls[k] = sidx < c.nsplit ? c.lse_part[(int64_t)sidx * rows + row] : kNegInf;
+    }
+#pragma unroll
+    for (int k = 0; k < SB; k++) mx = fmaxf(mx, ls[k]);
+  }
+  if (q == 0) s_mx[sp] = mx;
+  __syncthreads();
+#pragma unroll 1
+  for (int k = 0; k < SP; k++) mx = fmaxf(mx, s_mx[k]);
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  if (mx != kNegInf && q < tpr) {
+    for (int s0 = sp; s0 < c.nsplit; s0 += SB * SP) {
+      float ls[SB];
+      v4f o[SB];
+#pragma unroll
+      for (int k = 0; k < SB; k++) {
+        const int sidx = s0 + k * SP;
+        const bool in = sidx < c.nsplit;
+        ls[k] = in ? c.lse_part[(int64_t)sidx * rows + row] : kNegInf;
+        o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)sidx * rows + row) * c.dv + 4 * q)
+                  : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int k = 0; k < SB; k++) {
+        const float w = (ls[k] == kNegInf) ? 0.0f : __expf(ls[k] - mx);   // empty split: weight 0
+        den += w;
+        acc += w * o[k];
+      }
+    }
+  }
+  s_acc[sp][q] = acc;
+  if (q == 0) s_den[sp] = den;
+  __syncthreads();
+  if (sp != 0 || q >= tpr) return;
+  den = 0.0f;
+  acc = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 1
+  for (int k = 0; k < SP; k++) {
+    den += s_den[k];
+    acc += s_acc[k][q];
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  const int64_t ooff = (c.cu_q ? (int64_t)(q0 + i) * c.o_rs : (int64_t)b * c.o_bs + (int64_t)i * c.o_rs) +
+                       (int64_t)h * c.o_hs + 4 * q;
+  store4_half(reinterpret_cast<uint16_t*>(c.out) + ooff, acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
+              c.out_fp16 != 0);
+  if (c.lse && q == 0) {
+    const int64_t loff = c.cu_q ? (int64_t)h * c.l_hs + (int64_t)(q0 + i) * c.l_rs
+                                : (int64_t)b * c.l_bs + (int64_t)h * c.l_hs + (int64_t)i * c.l_rs;
+    c.lse[loff] = den > 0.0f ? mx + __logf(den) : kNegInf;
+  }
+}
+
 // KV tile of the prefill kernel: 128 keys when a two-stage tile pair fits twice in LDS, else 64.
 template <int D, int DV>
 constexpr int prefill_tile() { return (D + DV) <= 256 ? 128 : 64; }
@@ -1573,8 +1654,19 @@ int decode_units_per_split(const KParams& kp, int d, int dv) {
   if (hpw) return kp.batch * (kp.hkv / hpw);
   return kp.batch * kp.hkv * kp.nmb;
 }
+// Many splits over few rows: the row-per-workgroup kernel, whose split lanes load in parallel;
+// otherwise one thread per 4 output elements walking the splits.
 hipError_t launch_combine(const CParams& cp, hipStream_t stream) {
-  const int64_t threads = (int64_t)cp.batch * cp.max_sq * cp.hq * (cp.dv / 4);
+  const int64_t rows = (int64_t)cp.batch * cp.max_sq * cp.hq;
+  if (cp.nsplit > 16 && rows < (1 << 20)) {
+    const dim3 grid((unsigned)rows);
+    const int cg = cp.dv / 4;
+    if (cg <= 16) hipLaunchKernelGGL(fa8_combine_wide_kernel<16>, grid, dim3(1024), 0, stream, cp);
+    else if (cg <= 32) hipLaunchKernelGGL(fa8_combine_wide_kernel<32>, grid, dim3(1024), 0, stream, cp);
+    else hipLaunchKernelGGL(fa8_combine_wide_kernel<64>, grid, dim3(1024), 0, stream, cp);
+    return hipGetLastError();
+  }
+  const int64_t threads = rows * (cp.dv / 4);
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(fa8_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, cp);
   return hipGetLastError();

@@ -227,10 +227,12 @@ def test_long_kv_no_shrinkage():
         assert 0.99 <= ratio <= 1.01
 
 
-def test_combine_entry_point_alone():
-    # random partials with some empty splits, combined on the GPU vs the oracle's combine
+@pytest.mark.parametrize("S,DV", [(6, 128), (40, 128), (40, 96), (33, 256), (64, 64)])
+def test_combine_entry_point_alone(S, DV):
+    # random partials with some empty splits, combined on the GPU vs the oracle's combine (more
+    # than 16 splits take the split-parallel combine)
     rng = np.random.default_rng(1)
-    S, B, SQ, HQ, DV = 6, 3, 2, 4, 128
+    B, SQ, HQ = 3, 2, 4
     op = rng.standard_normal((S, B, SQ, HQ, DV)).astype(np.float32)
     lp = (rng.standard_normal((S, B, SQ, HQ)) * 3).astype(np.float32)
     lp[1] = -np.inf
