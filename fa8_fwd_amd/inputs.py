@@ -52,6 +52,7 @@ class AttnInputs:
     window_right: int = -1
     out_dtype: str = "bf16"                     # "bf16" | "fp16"
     name: str = ""
+    sink: Optional[np.ndarray] = None           # float32 [Hq] learnable sink logits, or None
 
     # --- per-batch lengths, resolved from whichever layout is in use ---
     def seqlens_q(self) -> np.ndarray:
@@ -174,6 +175,14 @@ def make_paged(seed: int, seqlens_k, heads_q: int, heads_kv: int, d: int, dv: in
                       page_size=page_size, q_descale=dq, k_descale=dk, v_descale=dvs,
                       softmax_scale=softmax_scale, causal=causal, window_left=window_left,
                       window_right=window_right, out_dtype=out_dtype, name=name)
+
+
+def with_sink(inp: AttnInputs, seed: int, mean: float = 0.0, std: float = 1.0) -> AttnInputs:
+    """A copy of inp with a learnable sink: one fp32 logit per query head, N(mean, std^2), drawn
+    from its own seeded generator (the other tensors are shared, not redrawn)."""
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn((inp.heads_q,), generator=g, dtype=torch.float32) * std + mean
+    return dataclasses.replace(inp, sink=z.numpy().astype(np.float32), name=inp.name + "_sink")
 
 
 def random_lengths(gen: torch.Generator, n: int, lo: int, hi: int) -> np.ndarray:

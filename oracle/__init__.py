@@ -55,6 +55,7 @@ class _Params(ctypes.Structure):
         ("q_descale", ctypes.c_void_p), ("k_descale", ctypes.c_void_p), ("v_descale", ctypes.c_void_p),
         ("softmax_scale", ctypes.c_double),
         ("causal", ctypes.c_int32), ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+        ("sink", ctypes.c_void_p),
     ]
 
 
@@ -123,7 +124,8 @@ def all_rows(inp):
     return np.concatenate(rb), np.concatenate(rh), np.concatenate(ri)
 
 
-def attention(inp, rows=None, key_range=None, threads: Optional[int] = None, softmax_scale: Optional[float] = None):
+def attention(inp, rows=None, key_range=None, threads: Optional[int] = None, softmax_scale: Optional[float] = None,
+              sink=None):
     """Exact fp64 attention for the requested rows.
 
     inp: an object with the fields of ``fa8_fwd_amd.inputs.AttnInputs`` (duck-typed).
@@ -179,6 +181,15 @@ def attention(inp, rows=None, key_range=None, threads: Optional[int] = None, sof
     p.softmax_scale = sc if sc and sc > 0 else 1.0 / math.sqrt(d)
     p.causal = 1 if inp.causal else 0
     p.window_left, p.window_right = int(inp.window_left), int(inp.window_right)
+    # learnable sink: one logit per query head joining the softmax denominator (``sink``
+    # overrides the input's own ``sink`` field, if any)
+    z = sink if sink is not None else getattr(inp, "sink", None)
+    if z is not None:
+        z = np.ascontiguousarray(np.asarray(z, np.float64).reshape(-1))
+        if z.size != Hq:
+            raise ValueError("sink must hold one logit per query head")
+        keep.append(z)
+    p.sink = _ptr(z)
     klo = khi = None
     if key_range is not None:
         klo = np.ascontiguousarray(np.asarray(key_range[0], np.int64))
@@ -205,14 +216,20 @@ def attention_full(inp, threads: Optional[int] = None):
     return o.reshape(B, S, Hq, dv), l.reshape(B, S, Hq).transpose(0, 2, 1).copy()
 
 
-def combine(o_parts: np.ndarray, lse_parts: np.ndarray):
+def combine(o_parts: np.ndarray, lse_parts: np.ndarray, sink=None):
     """Merge S split results: LSE = log sum_s exp(LSE_s); O = sum_s exp(LSE_s - LSE) O_s.
 
     o_parts: [S, ..., dv]; lse_parts: [S, ...] (natural log, -inf for an empty split).
     Rows where every split is empty give O = 0 and LSE = -inf. fp64 throughout.
+    sink: optional sink logit per row (broadcast to lse_parts.shape[1:]): it joins the
+    denominator as one more term with no value, i.e. a split with LSE = sink and O = 0.
     """
     o = np.asarray(o_parts, np.float64)
     l = np.asarray(lse_parts, np.float64)
+    if sink is not None:
+        z = np.broadcast_to(np.asarray(sink, np.float64), l.shape[1:])
+        o = np.concatenate([o, np.zeros((1,) + o.shape[1:])], axis=0)
+        l = np.concatenate([l, z[None]], axis=0)
     mx = np.max(l, axis=0)
     safe = np.where(np.isfinite(mx), mx, 0.0)
     w = np.exp(l - safe[None])                  # exp(-inf) = 0 for empty splits

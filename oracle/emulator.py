@@ -16,7 +16,15 @@ the order the pages give them, in numpy fp32 where the method works in fp32:
 5. l = alpha*l + sum(p)  (unrounded p by default);
 6. two-level PV: O_tile = P8 @ V for this tile alone, then O = alpha*O + O_tile (Design,
    "Two-level PV accumulation");
-7. end of a KV range: O = O * dv / l, LSE = ln2 * (m + log2 l - bias) (bias removed from the LSE).
+7. end of a KV range: O = O * dv / l, LSE = ln2 * (m + log2 l - bias) (bias removed from the LSE);
+8. learnable sink (optional, one logit z per query head, natural-log units): the page on the
+   sheared fp8 port (Summary) carries the 2^8 offset through the row sum and the sink term, so at
+   the end of the range z2 = z * log2 e enters the row sum with the same bias, after raising the
+   stored max to z2 when z2 is larger (a reading: the pages do not say how a sink above the row
+   max is handled; raising the max keeps every term below 2^bias):
+   m' = max(m, z2), l = 2^(m - m') l + 2^(z2 - m' + bias), O = 2^(m - m') O.
+   With ``sink_stage="combine"`` the sink is left out of each range and joins the combine as one
+   more term instead (the split-KV path: the partials hold no sink).
 
 Several splits over contiguous KV ranges are merged with ``oracle.combine``.
 """
@@ -70,7 +78,7 @@ def e4m3_encode_rne(x: np.ndarray, saturate: bool = True) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
-def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_splits: int = 1,
+def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_splits: int = 1, sink_stage: str = "finalize",
             l_from_rounded: bool = False, heads: Optional[list] = None, batches: Optional[list] = None,
             stats: Optional[dict] = None, interleave: int = 1, granule: Optional[int] = None):
     """Run the method on every query row of the selected (batch, head) pairs.
@@ -93,6 +101,8 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
     g = Hq // Hkv
     sq_all, sk_all = seqlens(inp)
     scale = inp.softmax_scale if inp.softmax_scale and inp.softmax_scale > 0 else 1.0 / math.sqrt(d)
+    zs = getattr(inp, "sink", None)
+    zs = None if zs is None else np.asarray(zs, np.float64).reshape(-1)
 
     def desc(x, b, kvh):
         if x is None:
@@ -174,6 +184,14 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
                     l = (alpha * l + psum.astype(np.float32)).astype(np.float32)
                     o_tile = (p8 @ vf[js]).astype(np.float32)
                     o = (alpha[:, None] * o + o_tile).astype(np.float32)
+                if zs is not None and sink_stage == "finalize":
+                    z2 = np.float32(zs[h] * LOG2E)
+                    mf = np.maximum(m, z2).astype(np.float32)
+                    with np.errstate(invalid="ignore"):
+                        a = np.where(np.isneginf(m), np.float32(0.0), np.exp2((m - mf).astype(np.float32))).astype(np.float32)
+                    l = (a * l + np.exp2((z2 - mf + np.float32(bias)).astype(np.float32))).astype(np.float32)
+                    o = (a[:, None] * o).astype(np.float32)
+                    m = mf
                 with np.errstate(divide="ignore", invalid="ignore"):
                     on = np.where(l[:, None] > 0, o.astype(np.float64) * dvs / l[:, None], 0.0)
                     ls = np.where(l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(np.where(l > 0, l, 1.0)) - bias), -np.inf)
@@ -185,10 +203,11 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
                           for i in range(0, len(parts_o), interleave)]
                 parts_o = [x[0] for x in merged]
                 parts_l = [x[1] for x in merged]
-            if num_splits == 1:
+            zc = float(zs[h]) if (zs is not None and sink_stage == "combine") else None
+            if num_splits == 1 and zc is None:
                 out[(b, h)] = (parts_o[0], parts_l[0])
             else:
-                out[(b, h)] = combine(np.stack(parts_o), np.stack(parts_l))
+                out[(b, h)] = combine(np.stack(parts_o), np.stack(parts_l), sink=zc)
     if stats is not None:
         stats["clipped"] = clipped
         stats["pmax"] = pmax

@@ -22,6 +22,14 @@
  *     O     = dv[b,kvh] * sum_J w_j v_j / l,    LSE = m + ln l   (natural log)
  *     J empty  ->  O = 0, LSE = -inf
  *
+ *   with a learnable sink (one logit z_h per query head, natural-log units, not scaled by the
+ *   softmax scale; listed among the supported features of the Hopper FP8 page, Summary, and
+ *   carried through the row sum by the sheared fp8 page, Summary): the sink joins the softmax
+ *   denominator and carries no value,
+ *     l     = sum_J exp(s_j - m) + exp(z_h - m),  m = max(max_J s_j, z_h)
+ *     O     = dv[b,kvh] * sum_J w_j v_j / l,    LSE = m + ln l
+ *     J empty  ->  O = 0, LSE = z_h
+ *
  * Note: every E4M3 value is an integer multiple of 2^-9 with magnitude <= 448 = 229376*2^-9,
  * so each product q_c*k_c is an integer multiple of 2^-18 below 2^36 * 2^-18 and any sum of up
  * to 256 of them stays below 2^44 * 2^-18: the dot product is exact in fp64 whatever the order.
@@ -80,6 +88,7 @@ typedef struct {
   const double* v_descale;
   double softmax_scale;
   int32_t causal, window_left, window_right;
+  const double* sink;          /* [Hq] sink logits, or NULL (no sink) */
 } fa8_oracle_params;
 
 static int64_t key_offset(const fa8_oracle_params* p, int b, int64_t j, int kvh, int is_v) {
@@ -106,8 +115,9 @@ static void one_row(const fa8_oracle_params* p, int b, int h, int i, int64_t klo
   if (p->window_left >= 0 && ip - p->window_left > lo) lo = ip - p->window_left;
   if (klo > lo) lo = klo;
   if (khi < hi) hi = khi;
+  const double z = p->sink ? p->sink[h] : -INFINITY;
   for (int c = 0; c < p->dv; c++) out[c] = 0.0;
-  if (hi <= lo) { *lse = -INFINITY; return; }
+  if (hi <= lo) { *lse = z; return; }
 
   double dq = p->q_descale ? p->q_descale[b * p->heads_kv + kvh] : 1.0;
   double dk = p->k_descale ? p->k_descale[b * p->heads_kv + kvh] : 1.0;
@@ -127,7 +137,8 @@ static void one_row(const fa8_oracle_params* p, int b, int h, int i, int64_t klo
     scores[j - lo] = s;
     if (s > m) m = s;
   }
-  double l = 0.0;
+  if (z > m) m = z;
+  double l = (z == -INFINITY) ? 0.0 : exp(z - m);
   for (int64_t j = lo; j < hi; j++) {
     double w = exp(scores[j - lo] - m);
     l += w;
