@@ -186,6 +186,8 @@ def decode_kernel_name(inp, dev, num_splits: int) -> str:
 
 def bench_prefill(inp, steps: int, warmup: int, dev):
     q, k, v, kw = device_args(inp, dev)
+    if getattr(inp, "sink", None) is not None:
+        kw["sink"] = to_dev(np.asarray(inp.sink, np.float32), dev)
     odt = torch.float16 if inp.out_dtype == "fp16" else torch.bfloat16
     out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=odt, device=dev)
     for _ in range(warmup):
@@ -207,8 +209,9 @@ def bench_prefill(inp, steps: int, warmup: int, dev):
 def other_workloads(args, dev) -> dict:
     """Figures of the remaining measured workloads, reported beside the headline (not part of
     `value`): long-KV decode (4 sequences of 131072 keys, 8/1 heads, 64-token pages; GB/s of the
-    decode step and of its kernel) and the mixed-shape varlen prefill (8 sequences, window 1024,
-    fp16 out; TFLOP/s of the visible pairs) for (d, dv) = (256, 256) and (192, 128)."""
+    decode step and of its kernel), the causal prefill workload with a learnable sink, and the
+    mixed-shape varlen prefill (8 sequences, window 1024, fp16 out; TFLOP/s of the visible pairs)
+    for (d, dv) = (256, 256) and (192, 128)."""
     out = {}
     lk = gen.long_kv_decode(3)
     ms, kms, S = bench_decode(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev)
@@ -217,6 +220,13 @@ def other_workloads(args, dev) -> dict:
                              "step_value": round(decode_step_bytes(lk) / (ms * 1e-3) / 1e9, 2),
                              "kernel_value": round(kb / (kms * 1e-3) / 1e9, 2), "kernel_ms": round(kms, 5),
                              "kernel_pct_of_hbm_peak": round(100 * kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    # the causal prefill workload with a learnable sink logit per query head (N(0, 1))
+    cs = gen.with_sink(gen.causal_prefill(2), 12)
+    ms, kms = bench_prefill(cs, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
+    fl = prefill_flop(cs)
+    out["causal_prefill_with_sink"] = {"workload": cs.name, "unit": "TFLOP/s",
+                                       "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
+                                       "kernel_pct_of_fp8_peak": round(100 * fl / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)}
     for d, dv in ((256, 256), (192, 128)):
         mv = gen.mixed_varlen(4, d=d, dv=dv)
         ms, kms = bench_prefill(mv, max(5, args.prefill_steps // 2), max(5, args.prefill_warmup // 5), dev)

@@ -54,6 +54,7 @@ class FwdParams(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("lse", ctypes.c_void_p),
         ("lse_batch_stride", ctypes.c_int64), ("lse_head_stride", ctypes.c_int64), ("lse_row_stride", ctypes.c_int64),
+        ("sink", ctypes.c_void_p),
     ]
 
 
@@ -77,7 +78,7 @@ def load():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.fa8_fwd_prefill.argtypes = [P, vp]
     lib.fa8_fwd_decode_splitkv.argtypes = [P, i32, vp, vp, vp]
-    lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp]
+    lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, vp]
     lib.fa8_check_params.argtypes = [P, i32]
     for f in ("fa8_fwd_prefill", "fa8_fwd_decode_splitkv", "fa8_combine", "fa8_check_params"):
         getattr(lib, f).restype = ctypes.c_int
@@ -110,6 +111,14 @@ def _fp8_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype == torch.float8_e4m3fn or t.dtype == torch.uint8:
         return t
     raise FA8Error(FA8_ERR_INVALID, f"{name} must be float8_e4m3fn (or its uint8 bytes), got {t.dtype}")
+
+
+def _sink_ptr(sink: Optional[torch.Tensor], heads_q: int) -> Optional[int]:
+    if sink is None:
+        return None
+    if sink.dtype != torch.float32 or sink.numel() != heads_q or (sink.dim() > 0 and sink.stride(-1) != 1):
+        raise FA8Error(FA8_ERR_INVALID, "sink must be a contiguous float32 tensor of heads_q logits")
+    return sink.data_ptr()
 
 
 def _descale(x: Optional[torch.Tensor], batch: int, heads_kv: int) -> Descale:
@@ -241,8 +250,9 @@ def prefill(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None, bl
             max_seqlen_q=None, max_seqlen_k=None, q_descale=None, k_descale=None, v_descale=None,
             softmax_scale: float = 0.0, causal: bool = False, window_left: int = -1, window_right: int = -1,
             out: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16, return_lse: bool = False,
-            lse: Optional[torch.Tensor] = None, stream=None):
-    """Full FP8 attention forward (fa8_fwd_prefill). Returns out, or (out, lse)."""
+            lse: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None, stream=None):
+    """Full FP8 attention forward (fa8_fwd_prefill). Returns out, or (out, lse). sink: optional
+    [heads_q] fp32 learnable sink logits."""
     lib = load()
     p = _params(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_k, block_table, max_seqlen_q, max_seqlen_k,
                 q_descale, k_descale, v_descale, softmax_scale, causal, window_left, window_right)
@@ -254,6 +264,7 @@ def prefill(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None, bl
     elif return_lse and lse is None:
         _, lse = _alloc_out(q, p.dv, out.dtype, varlen_q, True, p.batch, p.heads_q, p.max_seqlen_q)
     _set_out(p, out, lse, varlen_q)
+    p.sink = _sink_ptr(sink, p.heads_q)
     _check(lib.fa8_fwd_prefill(ctypes.byref(p), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
@@ -306,8 +317,8 @@ def decode_splitkv(q, k, v, *, num_splits: int, o_partial=None, lse_partial=None
 
 
 def combine(o_partial, lse_partial, *, batch: int, max_seqlen_q: int, heads_q: int, dv: int, out: torch.Tensor,
-            cu_seqlens_q=None, lse: Optional[torch.Tensor] = None, stream=None):
-    """LSE combine of split partials into out (fa8_combine)."""
+            cu_seqlens_q=None, lse: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None, stream=None):
+    """LSE combine of split partials into out (fa8_combine); sink: optional [heads_q] fp32 logits."""
     lib = load()
     S = o_partial.shape[0]
     varlen = cu_seqlens_q is not None
@@ -325,13 +336,14 @@ def combine(o_partial, lse_partial, *, batch: int, max_seqlen_q: int, heads_q: i
             lb, lh, lr = lse.stride(0), lse.stride(1), lse.stride(2)
     _check(lib.fa8_combine(o_partial.data_ptr(), lse_partial.data_ptr(), S, batch, max_seqlen_q, _ptr(cu_seqlens_q),
                            heads_q, dv, out.data_ptr(), ob, orow, oh, _OUT[out.dtype], _ptr(lse), lb, lh, lr,
-                           _stream(stream)))
+                           _sink_ptr(sink, heads_q), _stream(stream)))
     return out
 
 
 def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=torch.bfloat16, return_lse=False,
-           workspace: Optional[torch.Tensor] = None, stream=None, **kw):
-    """Split-KV decode followed by the combine. num_splits=None uses fa8_decode_num_splits_for."""
+           workspace: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None, stream=None, **kw):
+    """Split-KV decode followed by the combine. num_splits=None uses fa8_decode_num_splits_for; the
+    sink (optional [heads_q] fp32 logits) enters in the combine."""
     cu_q = kw.get("cu_seqlens_q")
     p = _params(q, k, v, cu_q, kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
                 kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), None, None, None, 0.0, False, -1, -1)
@@ -351,7 +363,8 @@ def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=tor
         out, lse = _alloc_out(q, DV, out_dtype, varlen, return_lse, B, HQ, SQ)
     else:
         lse = _alloc_out(q, DV, out.dtype, varlen, True, B, HQ, SQ)[1] if return_lse else None
-    combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=cu_q, lse=lse, stream=stream)
+    combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=cu_q, lse=lse, sink=sink,
+            stream=stream)
     return (out, lse) if return_lse else out
 
 

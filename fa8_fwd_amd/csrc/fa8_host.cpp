@@ -203,6 +203,7 @@ fa8::KParams make_kparams(const fa8_fwd_params* p) {
   k.out = p->out; k.o_bs = p->o_batch_stride; k.o_rs = p->o_row_stride; k.o_hs = p->o_head_stride;
   k.out_fp16 = p->out_dtype == FA8_OUT_FP16;
   k.lse = p->lse; k.l_bs = p->lse_batch_stride; k.l_hs = p->lse_head_stride; k.l_rs = p->lse_row_stride;
+  k.sink = p->sink;
   return k;
 }
 
@@ -324,7 +325,7 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
                        int32_t max_seqlen_q, const int32_t* cu_seqlens_q, int32_t heads_q, int32_t dv, void* out,
                        int64_t o_batch_stride, int64_t o_row_stride, int64_t o_head_stride, int32_t out_dtype,
                        float* lse, int64_t lse_batch_stride, int64_t lse_head_stride, int64_t lse_row_stride,
-                       void* stream) {
+                       const float* sink, void* stream) {
   if (num_splits < 1 || num_splits > FA8_MAX_SPLITS)
     return fail(FA8_ERR_INVALID, "num_splits %d outside 1..%d", num_splits, FA8_MAX_SPLITS);
   if (batch < 0 || max_seqlen_q < 0 || heads_q < 0 || max_seqlen_q >= kMaxLen || heads_q >= 65536 || batch >= 65536)
@@ -346,6 +347,7 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
   c.out = out; c.o_bs = o_batch_stride; c.o_rs = o_row_stride; c.o_hs = o_head_stride;
   c.out_fp16 = out_dtype == FA8_OUT_FP16;
   c.lse = lse; c.l_bs = lse_batch_stride; c.l_hs = lse_head_stride; c.l_rs = lse_row_stride;
+  c.sink = sink;
   hipError_t e = fa8::launch_combine(c, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA8_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -30,6 +30,7 @@ struct KParams {
   float* lse; int64_t l_bs, l_hs, l_rs;
   float* o_part; float* lse_part; int32_t nsplit;
   int32_t nmb;                // row blocks per (batch, head) (decode) or per (batch, q head) (prefill)
+  const float* sink;          // [hq] sink logits or null (prefill finalize only)
 };
 
 struct CParams {
@@ -39,6 +40,7 @@ struct CParams {
   const int32_t* cu_q;
   void* out; int64_t o_bs, o_rs, o_hs; int32_t out_fp16;
   float* lse; int64_t l_bs, l_hs, l_rs;
+  const float* sink;          // [hq] sink logits or null
 };
 
 // Rows per workgroup of the prefill kernel and of the decode kernel.

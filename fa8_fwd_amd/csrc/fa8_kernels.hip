@@ -49,6 +49,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr float kTau = 0.75f;    // lazy-rescale slack in log2 units, <= log2(448) - 8
 constexpr float kBias = 8.0f;    // P is computed as 2^(x - m + 8)
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // 1 KB read by the decode kernel's pipeline-filler loads (one 16-byte chunk per lane): a small
@@ -544,10 +545,22 @@ __device__ __forceinline__ void attn_tile16(const FA8_LDS uint8_t* kt, const FA8
 }
 
 // Final normalization and store of one lane's row (or its partial for split-KV decode).
+// Without SPLIT, a learnable sink logit z (p.sink) joins the row sum here with the same 2^8
+// offset as P: the stored max m rises to z2 = z log2 e when z2 is larger (alpha = 2^(m - m')
+// rescales l and O; every term stays below 2^8), then l += 2^(z2 - m' + 8). Split partials
+// leave the sink to the combine.
 template <int DV, bool SPLIT>
 __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[DV / 32], float m_run, float l_tot,
                                           float dvs, int hgrp, int b, int q0, int qi, int qh, int split) {
   constexpr int NB = DV / 32;
+  const float z2 = (!SPLIT && p.sink) ? p.sink[qh] * kLog2e : kNegInf;
+  if (z2 != kNegInf) {
+    const float mf = fmaxf(m_run, z2);
+    const float a = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - mf);
+    l_tot = a * l_tot + fast_exp2(z2 - mf + kBias);
+    dvs *= a;
+    m_run = mf;
+  }
   const bool nonempty = l_tot > 0.0f;
   const float inv = nonempty ? dvs / l_tot : 0.0f;
   const float lse = nonempty ? (m_run + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
@@ -1420,7 +1433,9 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   // splits in batches of 8 whose loads are all issued before any is used (the loop is bound by
   // memory latency, not bandwidth)
   constexpr int SB = 8;
-  float mx = kNegInf;
+  // a sink logit is one more denominator term without a value
+  const float z = c.sink ? c.sink[h] : kNegInf;
+  float mx = z;
   for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
     float ls[SB];
 #pragma unroll
@@ -1429,7 +1444,7 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
     for (int k = 0; k < SB; k++) mx = fmaxf(mx, ls[k]);
   }
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float den = 0.0f;
+  float den = (z == kNegInf) ? 0.0f : __expf(z - mx);
   if (mx != kNegInf) {
     for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
       float ls[SB];
@@ -1496,6 +1511,9 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
   }
   if (q == 0) s_mx[sp] = mx;
   __syncthreads();
+  // a sink logit is one more denominator term without a value (added once, below)
+  const float z = c.sink ? c.sink[h] : kNegInf;
+  mx = fmaxf(mx, z);
 #pragma unroll 1
   for (int k = 0; k < SP; k++) mx = fmaxf(mx, s_mx[k]);
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1524,7 +1542,7 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
   if (q == 0) s_den[sp] = den;
   __syncthreads();
   if (sp != 0 || q >= tpr) return;
-  den = 0.0f;
+  den = (z == kNegInf) ? 0.0f : __expf(z - mx);
   acc = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 1
   for (int k = 0; k < SP; k++) {

@@ -97,6 +97,14 @@ typedef struct {
  * lse (optional, fp32): natural-log log-sum-exp of the scaled scores per row, at
  *   lse[b * lse_batch_stride + h * lse_head_stride + i * lse_row_stride] (fixed length) or
  *   lse[h * lse_head_stride + (cu_seqlens_q[b] + i) * lse_row_stride] (varlen).
+ * sink (optional, device, [heads_q] fp32): a learnable sink logit z_h per query head, in
+ *   natural-log units (not multiplied by softmax_scale or the descales). It joins the softmax
+ *   denominator and carries no value: O = dv * sum_j e^{s_j} v_j / (sum_j e^{s_j} + e^{z_h}),
+ *   LSE = ln(sum_j e^{s_j} + e^{z_h}); a row with no visible key gets O = 0 and LSE = z_h
+ *   ("Native FP8 ... for Hopper", Summary, lists the learnable sink among the supported
+ *   features; the sheared fp8 page, Summary, carries the 2^8 P offset through the sink term).
+ *   fa8_fwd_prefill adds it at the end of each row; fa8_fwd_decode_splitkv leaves it out of the
+ *   partials and fa8_combine adds it once. NULL: no sink.
  * (d, dv) must be one of (64,64), (96,96), (128,128), (192,192), (256,256), (192,128)
  *   ("Native FP8 ... for Hopper", Supported); anything else is FA8_ERR_UNSUPPORTED.
  * Sizes: every dimension >= 0 (an empty problem launches nothing and returns FA8_OK); batch < 2^16;
@@ -125,6 +133,7 @@ typedef struct {
   int32_t out_dtype;               /* fa8_out_dtype */
   float* lse;                      /* optional */
   int64_t lse_batch_stride, lse_head_stride, lse_row_stride;
+  const float* sink;               /* optional, [heads_q] */
 } fa8_fwd_params;
 
 /*
@@ -163,14 +172,16 @@ fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, f
  * splits are all empty get O = 0 and LSE = -inf. The split-KV combine is part of each decode
  * step ("Native FP8 ... for Hopper", Performance). Layouts of o_partial / lse_partial as for
  * fa8_fwd_decode_splitkv; out/lse addressing as in fa8_fwd_params (cu_seqlens_q may be NULL
- * for fixed-length rows; lse may be NULL).
+ * for fixed-length rows; lse may be NULL). sink (optional, [heads_q] fp32, as in
+ * fa8_fwd_params): one more term e^{z_h} of the denominator with no value, i.e.
+ * LSE = log(sum_s exp(LSE_s) + exp(z_h)); rows with every split empty then get O = 0, LSE = z_h.
  */
 fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t num_splits,
                        int32_t batch, int32_t max_seqlen_q, const int32_t* cu_seqlens_q,
                        int32_t heads_q, int32_t dv, void* out, int64_t o_batch_stride,
                        int64_t o_row_stride, int64_t o_head_stride, int32_t out_dtype, float* lse,
                        int64_t lse_batch_stride, int64_t lse_head_stride, int64_t lse_row_stride,
-                       void* stream);
+                       const float* sink, void* stream);
 
 /* Runs the host-side validation of fa8_fwd_prefill (num_splits == 0) or of
  * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything. Needs no GPU. */

@@ -47,9 +47,14 @@ def out_dtype(inp):
     return torch.float16 if inp.out_dtype == "fp16" else torch.bfloat16
 
 
+def sink_tensor(inp):
+    z = getattr(inp, "sink", None)
+    return None if z is None else to_dev(np.asarray(z, np.float32))
+
+
 def run_prefill(inp, return_lse=True):
     q, k, v, kw = tensors(inp)
-    out, lse = binding.prefill(q, k, v, out_dtype=out_dtype(inp), return_lse=True, **kw)
+    out, lse = binding.prefill(q, k, v, out_dtype=out_dtype(inp), return_lse=True, sink=sink_tensor(inp), **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -63,7 +68,8 @@ def decode_schedule(inp, num_splits):
 
 def run_decode(inp, num_splits=None):
     q, k, v, kw = tensors(inp)
-    out, lse = binding.decode(q, k, v, num_splits=num_splits, out_dtype=out_dtype(inp), return_lse=True, **kw)
+    out, lse = binding.decode(q, k, v, num_splits=num_splits, out_dtype=out_dtype(inp), return_lse=True,
+                              sink=sink_tensor(inp), **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -222,7 +228,7 @@ LSE_METHOD = -math.log(1 - 2.0 ** -4) + 1e-4
 
 
 def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits=1, tile_n=GRANULE,
-                         interleave=1, granule=None):
+                         interleave=1, granule=None, sink_stage="finalize"):
     """Parity of one kernel result with the oracle.
 
     strict: every element within 2e-2 + 2e-2 |ref| (the stated tolerance), except elements where
@@ -244,7 +250,7 @@ def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits
     emu_o = emu_l = None
     if emu:
         emu_o, emu_l = emulate_full(inp, num_splits=num_splits, with_lse=True, tile_n=tile_n, interleave=interleave,
-                                    granule=granule)
+                                    granule=granule, sink_stage=sink_stage)
     n_method = 0
     if strict:
         bad = err > ATOL + RTOL * np.abs(ref)

@@ -126,8 +126,8 @@ def _decode_check(inp, num_splits, what, strict=True, emu=True):
     use_emu = emu and num_splits is not None and inp.window_left < 0
     ns = 1 if (num_splits is None or inp.window_left >= 0) else num_splits
     tile_n, inter = decode_schedule(inp, ns) if use_emu else (GRANULE, 1)
-    print(check_against_oracle(inp, got, glse, what, strict, use_emu, ns, tile_n, interleave=inter, granule=GRANULE),
-          flush=True)
+    print(check_against_oracle(inp, got, glse, what, strict, use_emu, ns, tile_n, interleave=inter, granule=GRANULE,
+                               sink_stage="combine"), flush=True)
     return got
 
 
@@ -247,3 +247,48 @@ def test_combine_entry_point_alone(S, DV):
     torch.cuda.synchronize()
     compare(out.float().cpu().numpy(), ref_o, "combine")
     compare_lse(lse.cpu().numpy(), ref_l.transpose(0, 2, 1), "combine lse")
+
+
+# ---- learnable sink (one logit per query head in the softmax denominator) ----
+
+@pytest.mark.parametrize("mean", [0.0, 6.0])
+def test_prefill_with_sink(mean):
+    # causal GQA with a ragged tail; mean 6 makes the sink a large share of each denominator
+    base = gen.make_dense(5, 2, 300, 517, 16, 2, 128, 128, causal=True, descales=(0.5, 0.5, 1.5))
+    inp = gen.with_sink(base, 8, mean=mean, std=1.0)
+    _prefill_check(inp, f"prefill with sink mean {mean}")
+
+
+def test_prefill_sink_empty_rows():
+    # Sq > Sk causal: rows without keys give O = 0 and LSE = the sink
+    inp = gen.with_sink(gen.make_dense(6, 1, 150, 70, 2, 1, 128, 128, causal=True), 9)
+    got, glse = run_prefill(inp)
+    _check(inp, got, glse, "prefill sink empty rows", strict=False)
+    assert np.all(got[0, :80] == 0)
+    np.testing.assert_allclose(glse[0, :, :80], np.broadcast_to(inp.sink[:, None], (2, 80)), rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, None])
+def test_decode_paged_with_sink(num_splits):
+    inp = gen.with_sink(gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096), 10, mean=4.0, std=2.0)
+    _decode_check(inp, num_splits, f"paged decode with sink splits={num_splits}")
+
+
+@pytest.mark.parametrize("S", [6, 40])
+def test_combine_with_sink(S):
+    rng = np.random.default_rng(2)
+    B, SQ, HQ, DV = 3, 2, 4, 128
+    op = rng.standard_normal((S, B, SQ, HQ, DV)).astype(np.float32)
+    lp = (rng.standard_normal((S, B, SQ, HQ)) * 3).astype(np.float32)
+    lp[:, 2, 1, 3] = -np.inf          # a row with every split empty: O = 0, LSE = the sink
+    z = np.array([0.5, -1.0, 2.0, 8.0], np.float32)
+    ref_o, ref_l = oracle.combine(op, lp, sink=z[None, None, :])
+    dev = torch.device("cuda:0")
+    out = torch.empty((B, SQ, HQ, DV), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, HQ, SQ), dtype=torch.float32, device=dev)
+    binding.combine(torch.from_numpy(op).to(dev), torch.from_numpy(lp).to(dev), batch=B, max_seqlen_q=SQ,
+                    heads_q=HQ, dv=DV, out=out, lse=lse, sink=torch.from_numpy(z).to(dev))
+    torch.cuda.synchronize()
+    compare(out.float().cpu().numpy(), ref_o, "combine with sink")
+    compare_lse(lse.cpu().numpy(), ref_l.transpose(0, 2, 1), "combine with sink lse")
+    assert np.all(out.float().cpu().numpy()[2, 1, 3] == 0)
