@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from oracle import emulator
+from oracle import emulator, quant
 from fa8_fwd_amd import inputs as gen
 
 E4M3 = torch.float8_e4m3fn
@@ -550,3 +550,77 @@ def test_emulator_with_sink_tracks_oracle(oracle_lib):
     for stage, ns in (("finalize", 1), ("combine", 3)):
         e = rel_err(inp, ns, stage)
         assert e <= 1.3 * e0 + 1e-3, (stage, e, e0)
+
+
+# ----------------------------------------------------------------------------------------
+# Q quantizer (per (batch, kv head) block: scale = amax / 448, codes = E4M3(x / scale))
+# ----------------------------------------------------------------------------------------
+
+def _bf16_values(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(torch.bfloat16).float().numpy()
+
+
+def test_quantizer_block_max_maps_to_448(oracle_lib):
+    q = _bf16_values((2, 40, 8, 64), 1, 3.0)
+    codes, s = quant.quantize_q(q, heads_kv=2)
+    dec = oracle.e4m3_table()[codes]
+    for b in range(2):
+        for kvh in range(2):
+            blk = q[b, :, kvh * 4:(kvh + 1) * 4]
+            d = dec[b, :, kvh * 4:(kvh + 1) * 4]
+            assert s[b, kvh] == np.float32(np.abs(blk).max() / np.float32(448))
+            # the block maximum maps to +-448; so does nothing below 432 (half the 32-wide step
+            # under 448 away)
+            assert np.all(np.abs(d)[np.abs(blk) == np.abs(blk).max()] == 448.0)
+            y = np.abs(blk) / s[b, kvh]
+            assert np.all(y[np.abs(d) == 448.0] >= 432.0)
+
+
+def test_quantizer_exact_on_representable_inputs(oracle_lib):
+    # x = 2^k * (E4M3 values) with one value at 448: scale = 2^k exactly, codes are the inputs'
+    table = oracle.e4m3_table()
+    rng = np.random.default_rng(3)
+    want = rng.integers(0, 256, size=(1, 17, 4, 32)).astype(np.uint8)
+    want[np.isnan(table[want])] = 0x38
+    want[0, 0, 0, 0] = 0x7E                       # 448: the block maximum
+    x = (table[want] * 2.0 ** -5).astype(np.float32)
+    codes, s = quant.quantize_q(x, heads_kv=1)
+    assert s[0, 0] == np.float32(2.0 ** -5)
+    # equal values may take either sign of zero; compare decoded values
+    assert np.array_equal(table[codes], table[want])
+
+
+def test_quantizer_power_of_two_scaling_invariance(oracle_lib):
+    # scaling a block by 2^k scales its descale by 2^k and leaves its codes unchanged
+    q = _bf16_values((3, 25, 8, 128), 4)
+    c1, s1 = quant.quantize_q(q, heads_kv=4)
+    q2 = q.copy()
+    q2[1] *= 8.0
+    c2, s2 = quant.quantize_q(q2, heads_kv=4)
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(s2[1], s1[1] * 8) and np.array_equal(s2[[0, 2]], s1[[0, 2]])
+
+
+def test_quantizer_error_within_half_step(oracle_lib):
+    # |dec(code) - x / s| <= half the E4M3 spacing at that magnitude (2^(e-4), subnormal 2^-10),
+    # and the codes are monotone in x
+    q = _bf16_values((1, 64, 2, 128), 5, 0.1)
+    codes, s = quant.quantize_q(q, heads_kv=1)
+    y = (q / s[0, 0]).astype(np.float64)
+    d = oracle.e4m3_table()[codes]
+    e = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6)))
+    assert np.all(np.abs(d - y) <= 2.0 ** (e - 4) + 1e-12)
+    order = np.argsort(y.reshape(-1), kind="stable")
+    assert np.all(np.diff(d.reshape(-1)[order]) >= 0)
+
+
+def test_quantizer_zero_block_and_varlen(oracle_lib):
+    q = _bf16_values((30, 4, 64), 6)
+    cu = np.array([0, 10, 10, 30], np.int32)          # one empty sequence
+    q[:10, 2:] = 0.0                                  # batch 0, kv head 1: all zeros
+    codes, s = quant.quantize_q(q, heads_kv=2, cu_seqlens_q=cu)
+    assert s[0, 1] == 1.0 and np.all(codes[:10, 2:] == 0)
+    assert np.all(s[1] == 1.0)                         # the empty sequence
+    ref, rs = quant.quantize_q(q[10:30][None], heads_kv=2)
+    assert np.array_equal(codes[10:30], ref[0]) and np.array_equal(s[2], rs[0])
