@@ -227,6 +227,27 @@ def other_workloads(args, dev) -> dict:
     out["causal_prefill_with_sink"] = {"workload": cs.name, "unit": "TFLOP/s",
                                        "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
                                        "kernel_pct_of_fp8_peak": round(100 * fl / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)}
+    # the Q quantizer (the step before the path) on the causal prefill workload's Q, from bf16
+    gq = torch.Generator().manual_seed(13)
+    qb = torch.randn((2, 8192, 32, 128), generator=gq).to(torch.bfloat16).to(dev)
+    q8 = torch.empty(qb.shape, dtype=torch.uint8, device=dev)
+    qs = torch.empty((2, 8), dtype=torch.float32, device=dev)
+    for _ in range(10):
+        binding.quantize_q(qb, 8, out=q8, descale=qs)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        binding.quantize_q(qb, 8, out=q8, descale=qs)
+        b.record()
+    torch.cuda.synchronize()
+    qms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    qbytes = qb.numel() * 3 + qs.numel() * 4          # bf16 read once, E4M3 written once, descales
+    out["q_quantize_causal_prefill"] = {"workload": "q bf16 [2, 8192, 32, 128], 8 kv heads", "unit": "GB/s",
+                                        "kernel_value": round(qbytes / (qms * 1e-3) / 1e9, 2), "kernel_ms": round(qms, 5),
+                                        "kernel_pct_of_hbm_peak": round(100 * qbytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                                        "note": "two launches (block maxima, then codes): Q is read twice"}
+    del qb, q8
     for d, dv in ((256, 256), (192, 128)):
         mv = gen.mixed_varlen(4, d=d, dv=dv)
         ms, kms = bench_prefill(mv, max(5, args.prefill_steps // 2), max(5, args.prefill_warmup // 5), dev)

@@ -65,6 +65,20 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+class QuantParams(ctypes.Structure):
+    """fa8_quant_params of include/fa8.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("in_dtype", ctypes.c_int32),
+        ("q_batch_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64), ("q_head_stride", ctypes.c_int64),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("q_out", ctypes.c_void_p),
+        ("o_batch_stride", ctypes.c_int64), ("o_row_stride", ctypes.c_int64), ("o_head_stride", ctypes.c_int64),
+        ("q_descale", ctypes.c_void_p),
+    ]
+
+
 def load():
     """Load libfa8.so (built in-tree by fa8_fwd_amd.build); raise if it is missing."""
     global _lib
@@ -80,6 +94,11 @@ def load():
     lib.fa8_fwd_decode_splitkv.argtypes = [P, i32, vp, vp, vp]
     lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, vp]
     lib.fa8_check_params.argtypes = [P, i32]
+    QP = ctypes.POINTER(QuantParams)
+    lib.fa8_quantize_q_workspace_bytes.argtypes = [QP]
+    lib.fa8_quantize_q_workspace_bytes.restype = ctypes.c_int64
+    lib.fa8_quantize_q.argtypes = [QP, vp, vp]
+    lib.fa8_quantize_q.restype = ctypes.c_int
     for f in ("fa8_fwd_prefill", "fa8_fwd_decode_splitkv", "fa8_combine", "fa8_check_params"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fa8_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -388,3 +407,49 @@ def last_error() -> str:
 
 def version() -> str:
     return load().fa8_version().decode()
+
+
+def quantize_q(q: torch.Tensor, heads_kv: int, *, cu_seqlens_q=None, max_seqlen_q: Optional[int] = None,
+               out: Optional[torch.Tensor] = None, descale: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None):
+    """Per-(batch, kv head) E4M3 quantization of a bf16/fp16 Q (fa8_quantize_q). Returns
+    (q_fp8 as uint8 with q's shape, descale [batch, heads_kv] fp32)."""
+    lib = load()
+    if q.dtype not in _OUT:
+        raise FA8Error(FA8_ERR_INVALID, "q must be bfloat16 or float16")
+    p = QuantParams()
+    varlen = cu_seqlens_q is not None
+    if varlen:
+        if q.dim() != 3:
+            raise FA8Error(FA8_ERR_INVALID, "varlen q must be [total_q, heads_q, d]")
+        batch = cu_seqlens_q.numel() - 1
+        if max_seqlen_q is None:
+            raise FA8Error(FA8_ERR_INVALID, "varlen q needs max_seqlen_q")
+        p.q_batch_stride, p.q_row_stride, p.q_head_stride = 0, q.stride(0), q.stride(1)
+        hq, d = q.shape[1], q.shape[2]
+    else:
+        if q.dim() != 4:
+            raise FA8Error(FA8_ERR_INVALID, "q must be [batch, seqlen_q, heads_q, d]")
+        batch, sq, hq, d = q.shape
+        max_seqlen_q = sq if max_seqlen_q is None else max_seqlen_q
+        p.q_batch_stride, p.q_row_stride, p.q_head_stride = q.stride(0), q.stride(1), q.stride(2)
+    if q.stride(-1) != 1:
+        raise FA8Error(FA8_ERR_INVALID, "q's last dimension must be contiguous")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.uint8, device=q.device)
+    if descale is None:
+        descale = torch.empty((batch, heads_kv), dtype=torch.float32, device=q.device)
+    if varlen:
+        p.o_batch_stride, p.o_row_stride, p.o_head_stride = 0, out.stride(0), out.stride(1)
+    else:
+        p.o_batch_stride, p.o_row_stride, p.o_head_stride = out.stride(0), out.stride(1), out.stride(2)
+    p.batch, p.heads_q, p.heads_kv, p.d, p.max_seqlen_q = batch, hq, heads_kv, d, int(max_seqlen_q)
+    p.q, p.in_dtype, p.cu_seqlens_q = q.data_ptr(), _OUT[q.dtype], _ptr(cu_seqlens_q)
+    p.q_out, p.q_descale = out.data_ptr(), descale.data_ptr()
+    nbytes = int(lib.fa8_quantize_q_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise FA8Error(FA8_ERR_INVALID, "workspace too small")
+    _check(lib.fa8_quantize_q(ctypes.byref(p), workspace.data_ptr(), _stream(stream)))
+    return out, descale

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa8.so")
-SOURCES = ["fa8_host.cpp", "fa8_kernels.hip"]
+SOURCES = ["fa8_host.cpp", "fa8_kernels.hip", "fa8_quant.hip"]
 
 # Packed-fp32 VALU forms are turned off for every HIP translation unit.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

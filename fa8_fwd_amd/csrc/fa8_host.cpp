@@ -354,3 +354,58 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
 }
 
 }  // extern "C"
+
+// ---- Q quantizer ----
+namespace {
+fa8_status validate_quant(const fa8_quant_params* p) {
+  if (!p) return fail(FA8_ERR_INVALID, "params is NULL");
+  if (p->batch < 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->max_seqlen_q < 0)
+    return fail(FA8_ERR_INVALID, "batch, heads and max_seqlen_q must be non-negative (heads > 0)");
+  if (p->heads_q % p->heads_kv) return fail(FA8_ERR_INVALID, "heads_q must be a multiple of heads_kv");
+  if (!(p->d == 64 || p->d == 96 || p->d == 128 || p->d == 192 || p->d == 256))
+    return fail(FA8_ERR_UNSUPPORTED, "head dim %d is not supported", p->d);
+  if (p->in_dtype != FA8_OUT_BF16 && p->in_dtype != FA8_OUT_FP16)
+    return fail(FA8_ERR_INVALID, "in_dtype must be FA8_OUT_BF16 or FA8_OUT_FP16");
+  if (p->batch >= (1 << 16) || p->heads_q >= (1 << 16) || (int64_t)p->max_seqlen_q >= kMaxLen)
+    return fail(FA8_ERR_INVALID, "sizes out of range");
+  if (p->batch == 0 || p->max_seqlen_q == 0) return FA8_OK;
+  if (!p->q || !p->q_out || !p->q_descale) return fail(FA8_ERR_INVALID, "q, q_out and q_descale must be non-NULL");
+  if (!aligned(p->q, 16) || !aligned(p->q_out, 8) || !aligned(p->q_descale, 4))
+    return fail(FA8_ERR_INVALID, "q must be 16-byte, q_out 8-byte and q_descale 4-byte aligned");
+  if ((p->q_row_stride | p->q_head_stride | (p->cu_seqlens_q ? 0 : p->q_batch_stride)) % 8)
+    return fail(FA8_ERR_INVALID, "q strides must be multiples of 8 elements");
+  if ((p->o_row_stride | p->o_head_stride | (p->cu_seqlens_q ? 0 : p->o_batch_stride)) % 8)
+    return fail(FA8_ERR_INVALID, "q_out strides must be multiples of 8 bytes");
+  if (p->q_row_stride < 0 || p->q_head_stride < 0 || p->q_batch_stride < 0 || p->o_row_stride < 0 ||
+      p->o_head_stride < 0 || p->o_batch_stride < 0)
+    return fail(FA8_ERR_INVALID, "strides must be non-negative");
+  return FA8_OK;
+}
+int64_t quant_chunks(const fa8_quant_params* p) { return ((int64_t)p->max_seqlen_q + fa8::kQuantRows - 1) / fa8::kQuantRows; }
+}  // namespace
+
+extern "C" int64_t fa8_quantize_q_workspace_bytes(const fa8_quant_params* p) {
+  if (!p || p->batch <= 0 || p->heads_kv <= 0 || p->max_seqlen_q <= 0) return 0;
+  return (int64_t)p->batch * p->heads_kv * quant_chunks(p) * (int64_t)sizeof(float);
+}
+
+extern "C" fa8_status fa8_quantize_q(const fa8_quant_params* p, void* workspace, void* stream) {
+  fa8_status st = validate_quant(p);
+  if (st != FA8_OK) return st;
+  if (p->batch == 0 || p->max_seqlen_q == 0) return ok();
+  if (!workspace || !aligned(workspace, 4)) return fail(FA8_ERR_INVALID, "workspace must be non-NULL and 4-byte aligned");
+  const int64_t nchunk = quant_chunks(p);
+  if (nchunk >= ((int64_t)1 << 31)) return fail(FA8_ERR_INVALID, "max_seqlen_q too large");
+  fa8::QParams q{};
+  q.q = p->q; q.q_bs = p->q_batch_stride; q.q_rs = p->q_row_stride; q.q_hs = p->q_head_stride;
+  q.in_fp16 = p->in_dtype == FA8_OUT_FP16;
+  q.cu_q = p->cu_seqlens_q;
+  q.q_out = p->q_out; q.o_bs = p->o_batch_stride; q.o_rs = p->o_row_stride; q.o_hs = p->o_head_stride;
+  q.descale = p->q_descale;
+  q.ws = (float*)workspace;
+  q.batch = p->batch; q.max_sq = p->max_seqlen_q; q.hkv = p->heads_kv; q.g = p->heads_q / p->heads_kv;
+  q.d = p->d; q.nchunk = (int32_t)nchunk;
+  hipError_t e = fa8::launch_quantize_q(q, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA8_ERR_HIP, "quantizer launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -43,6 +43,18 @@ struct CParams {
   const float* sink;          // [hq] sink logits or null
 };
 
+// Q quantizer: one chunk = kQuantRows rows of one (batch, kv head) block.
+struct QParams {
+  const void* q; int64_t q_bs, q_rs, q_hs; int32_t in_fp16;   // strides in elements
+  const int32_t* cu_q;
+  void* q_out; int64_t o_bs, o_rs, o_hs;                      // strides in bytes
+  float* descale;                                             // [batch, hkv]
+  float* ws;                                                  // [batch, hkv, nchunk]
+  int32_t batch, max_sq, hkv, g, d, nchunk;
+};
+constexpr int kQuantRows = 32;
+hipError_t launch_quantize_q(const QParams& qp, hipStream_t stream);
+
 // Rows per workgroup of the prefill kernel and of the decode kernel.
 constexpr int kPrefillRows = 128;
 constexpr int kDecodeRows = 32;

@@ -1,0 +1,150 @@
+// Per-(batch, kv head) FP8 quantization of a bf16/fp16 Q: the step before the attention path.
+// The block quantization formula of the FlashAttention-3 page ("Low-Precision FP8 Attention
+// with Block Scaling"): scale = max|X_block| / 448, X_fp8 = clip(round(X / scale), -448, 448),
+// with the block = every query row of one sequence and the q heads of one kv head, which is the
+// granularity of the attention path's q descale. Each code is decided in fp32: s = amax / 448
+// (1 for a block of zeros), y = x / s (IEEE division), clip to [-448, 448], round to nearest
+// even E4M3.
+//
+// Two launches over chunks of kQuantRows rows of one (batch, kv head): the first writes each
+// chunk's max |x| to the workspace, the second reduces the chunk maxima of its block, writes the
+// descale (chunk 0) and quantizes its chunk. HBM-bound: Q is read twice, the codes written once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa8_internal.h"
+
+namespace fa8 {
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+
+// 8 consecutive input elements (16 bytes) as fp32
+__device__ __forceinline__ void load8(const void* base, int64_t off, bool fp16, float (&x)[8]) {
+  const v4i w = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(base) + off);
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t u = (uint32_t)w[i];
+    if (fp16) {
+      x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFF));
+      x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+    } else {
+      x[2 * i] = __builtin_bit_cast(float, u << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, u & 0xFFFF0000u);
+    }
+  }
+}
+
+struct Chunk {
+  int64_t in_row0;    // element offset of the chunk's first row, head kvh * g
+  int64_t out_row0;   // byte offset of the same
+  int rows;           // rows of the chunk inside the sequence (0 .. kQuantRows)
+};
+
+__device__ __forceinline__ Chunk chunk_of(const QParams& p, int b, int kvh, int c) {
+  const int q0 = p.cu_q ? p.cu_q[b] : 0;
+  const int sq = p.cu_q ? p.cu_q[b + 1] - q0 : p.max_sq;
+  const int r0 = c * kQuantRows;
+  Chunk ch;
+  ch.rows = max(0, min(sq - r0, kQuantRows));
+  const int64_t row = p.cu_q ? (int64_t)q0 + r0 : (int64_t)r0;
+  ch.in_row0 = (p.cu_q ? 0 : (int64_t)b * p.q_bs) + row * p.q_rs + (int64_t)kvh * p.g * p.q_hs;
+  ch.out_row0 = (p.cu_q ? 0 : (int64_t)b * p.o_bs) + row * p.o_rs + (int64_t)kvh * p.g * p.o_hs;
+  return ch;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); w++) v = fmaxf(v, red[w]);
+  return v;
+}
+
+}  // namespace
+
+// grid (chunks, heads_kv, batch), 256 threads: max |x| of each chunk -> ws[(b hkv + kvh) chunks + c]
+__global__ void __launch_bounds__(256) fa8_quant_amax_kernel(const QParams p) {
+  __shared__ float red[4];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const Chunk ch = chunk_of(p, b, kvh, c);
+  const int vpr = p.g * (p.d / 8);                 // 8-element vectors per row of the block
+  const int nv = ch.rows * vpr;
+  const bool fp16 = p.in_fp16 != 0;
+  float m = 0.0f;
+  // four vectors per thread and pass, their loads issued together
+  constexpr int U = 4;
+  for (int v0 = threadIdx.x; v0 < nv; v0 += U * blockDim.x) {
+    float x[U][8];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int v = v0 + u * blockDim.x;
+      if (v < nv) {
+        const int r = v / vpr, rem = v - r * vpr;
+        const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
+        load8(p.q, ch.in_row0 + (int64_t)r * p.q_rs + (int64_t)h * p.q_hs + col, fp16, x[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) x[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++)
+#pragma unroll
+      for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x[u][i]));
+  }
+  m = block_max(m, red);
+  if (threadIdx.x == 0) p.ws[((int64_t)b * p.hkv + kvh) * p.nchunk + c] = m;
+}
+
+// grid (chunks, heads_kv, batch), 256 threads: block descale and E4M3 codes of the chunk
+__global__ void __launch_bounds__(256) fa8_quant_apply_kernel(const QParams p) {
+  __shared__ float red[4];
+  const int c = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const float* part = p.ws + ((int64_t)b * p.hkv + kvh) * p.nchunk;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < p.nchunk; i += blockDim.x) m = fmaxf(m, part[i]);
+  const float amax = block_max(m, red);
+  const float s = amax > 0.0f ? amax / kE4M3Max : 1.0f;
+  if (c == 0 && threadIdx.x == 0) p.descale[(int64_t)b * p.hkv + kvh] = s;
+  const Chunk ch = chunk_of(p, b, kvh, c);
+  const int vpr = p.g * (p.d / 8);
+  const int nv = ch.rows * vpr;
+  const bool fp16 = p.in_fp16 != 0;
+#pragma unroll 4
+  for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+    const int r = v / vpr, rem = v - r * vpr;
+    const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
+    float x[8];
+    load8(p.q, ch.in_row0 + (int64_t)r * p.q_rs + (int64_t)h * p.q_hs + col, fp16, x);
+    int w[2];
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+      float y[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) y[i] = fminf(fmaxf(x[4 * k + i] / s, -kE4M3Max), kE4M3Max);
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+    }
+    uint8_t* dst = reinterpret_cast<uint8_t*>(p.q_out) + ch.out_row0 + (int64_t)r * p.o_rs + (int64_t)h * p.o_hs + col;
+    *reinterpret_cast<v2i*>(dst) = (v2i){w[0], w[1]};
+  }
+}
+
+hipError_t launch_quantize_q(const QParams& qp, hipStream_t stream) {
+  const dim3 grid((unsigned)qp.nchunk, (unsigned)qp.hkv, (unsigned)qp.batch);
+  hipLaunchKernelGGL(fa8_quant_amax_kernel, grid, dim3(256), 0, stream, qp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fa8_quant_apply_kernel, grid, dim3(256), 0, stream, qp);
+  return hipGetLastError();
+}
+
+}  // namespace fa8

@@ -183,6 +183,35 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
                        int64_t lse_batch_stride, int64_t lse_head_stride, int64_t lse_row_stride,
                        const float* sink, void* stream);
 
+/*
+ * Per-(batch, kv head) FP8 quantization of a bf16 or fp16 Q, the step before the attention path
+ * (the block quantization formula of the FlashAttention-3 page, "Low-Precision FP8 Attention
+ * with Block Scaling": scale = max|X_block| / 448, X_fp8 = clip(round(X / scale), -448, 448)).
+ * The block is every query row of sequence b and the q heads h with h / (heads_q / heads_kv)
+ * == kvh, the granularity of fa8_fwd_params.q_descale. Each code is decided in fp32:
+ * s = amax / 448 (s = 1 for a block of zeros or an empty sequence), y = x / s (IEEE division),
+ * clip to [-448, 448], round to nearest even E4M3FN. Outputs: q_out (E4M3 bytes, its own
+ * strides) and q_descale[b * heads_kv + kvh] = s, ready to pass as a (batch, kv_heads) descale.
+ * q: [batch, max_seqlen_q, heads_q, d] (strides in elements) or varlen [total_q, heads_q, d] with
+ * cu_seqlens_q; in_dtype: FA8_OUT_BF16 or FA8_OUT_FP16 (the element type of q). d must be one of
+ * the supported head dims; q, q_out and their row and head strides 16-byte / 8-byte aligned.
+ * workspace: fa8_quantize_q_workspace_bytes(p) bytes of device memory (4-byte aligned), caller
+ * owned, contents irrelevant on entry. Two launches on stream; nothing is allocated.
+ */
+typedef struct {
+  int32_t batch, heads_q, heads_kv, d, max_seqlen_q;
+  const void* q;
+  int32_t in_dtype;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;    /* elements */
+  const int32_t* cu_seqlens_q;
+  void* q_out;
+  int64_t o_batch_stride, o_row_stride, o_head_stride;    /* bytes */
+  float* q_descale;                                       /* [batch, heads_kv] */
+} fa8_quant_params;
+
+int64_t fa8_quantize_q_workspace_bytes(const fa8_quant_params* p);
+fa8_status fa8_quantize_q(const fa8_quant_params* p, void* workspace, void* stream);
+
 /* Runs the host-side validation of fa8_fwd_prefill (num_splits == 0) or of
  * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything. Needs no GPU. */
 fa8_status fa8_check_params(const fa8_fwd_params* p, int32_t num_splits);

@@ -207,3 +207,22 @@ def test_decode_plan(monkeypatch):
     monkeypatch.delenv("FA8_DECODE_KERNEL")
     with pytest.raises(binding.FA8Error):
         binding.decode_plan(q, k, v, num_splits=0, **kw)
+
+
+def test_quantize_q_host_validation():
+    # argument errors are reported before any launch (no GPU needed)
+    import ctypes
+    from fa8_fwd_amd import binding
+    lib = binding.load()
+    p = binding.QuantParams()
+    p.batch, p.heads_q, p.heads_kv, p.d, p.max_seqlen_q = 2, 6, 4, 128, 16   # 6 % 4 != 0
+    p.in_dtype = binding.FA8_OUT_BF16
+    assert lib.fa8_quantize_q(ctypes.byref(p), None, None) == binding.FA8_ERR_INVALID
+    p.heads_q, p.d = 8, 80
+    assert lib.fa8_quantize_q(ctypes.byref(p), None, None) == binding.FA8_ERR_UNSUPPORTED
+    p.d, p.in_dtype = 128, 7
+    assert lib.fa8_quantize_q(ctypes.byref(p), None, None) == binding.FA8_ERR_INVALID
+    p.in_dtype, p.batch = binding.FA8_OUT_FP16, 0          # empty problem: nothing to do
+    assert lib.fa8_quantize_q(ctypes.byref(p), None, None) == binding.FA8_OK
+    p.batch = 3
+    assert lib.fa8_quantize_q_workspace_bytes(ctypes.byref(p)) == 3 * 4 * 1 * 4   # 16 rows: one 32-row chunk

@@ -1,0 +1,65 @@
+"""GPU parity of the Q quantizer (fa8_quantize_q) with the oracle's quantizer: every E4M3 code
+and every descale bit for bit (integer and byte work), bf16 and fp16 inputs, dense and varlen
+layouts, decode and prefill shapes, and a quantized Q run through the prefill path."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quant
+from fa8_fwd_amd import binding
+from fa8_fwd_amd import inputs as gen
+
+from helpers import check_against_oracle, prefill_tile, tensors
+
+pytestmark = pytest.mark.gpu
+
+
+def _q(shape, seed, dtype, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape,hkv", [((2, 300, 16, 128), 2), ((64, 1, 32, 128), 8), ((3, 77, 8, 64), 8),
+                                       ((1, 40, 6, 256), 3), ((2, 33, 4, 96), 1), ((1, 17, 4, 192), 2)])
+def test_quantizer_bit_exact_dense(dtype, shape, hkv):
+    q = _q(shape, 1, dtype, 2.0)
+    q[0, 0, 0, 0] = -0.0
+    dev = torch.device("cuda:0")
+    got, s = binding.quantize_q(q.to(dev), hkv)
+    torch.cuda.synchronize()
+    ref, rs = quant.quantize_q(q.float().numpy(), hkv)
+    assert np.array_equal(got.cpu().numpy(), ref), f"{int((got.cpu().numpy() != ref).sum())} codes differ"
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantizer_bit_exact_varlen_with_zero_and_empty_blocks():
+    q = _q((120, 8, 128), 2, torch.float16, 0.05)
+    cu = torch.tensor([0, 50, 50, 97, 120], dtype=torch.int32)
+    q[50:97, 4:] = 0.0                                   # batch 2, kv head 1: a block of zeros
+    dev = torch.device("cuda:0")
+    got, s = binding.quantize_q(q.to(dev), 2, cu_seqlens_q=cu.to(dev), max_seqlen_q=50)
+    torch.cuda.synchronize()
+    ref, rs = quant.quantize_q(q.float().numpy(), 2, cu_seqlens_q=cu.numpy())
+    assert np.array_equal(got.cpu().numpy(), ref)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert s.cpu().numpy()[1].tolist() == [1.0, 1.0] and s.cpu().numpy()[2, 1] == 1.0
+
+
+def test_quantized_q_through_prefill():
+    # bf16 Q quantized on the GPU, then the FP8 prefill with the produced per-(b, kv head) descale,
+    # against the oracle on the same codes and descales
+    base = gen.make_dense(30, 2, 200, 333, 8, 2, 128, 128, causal=True, descales=(None, 0.5, 1.5))
+    qb = _q((2, 200, 8, 128), 3, torch.bfloat16, 0.3)
+    dev = torch.device("cuda:0")
+    codes, s = binding.quantize_q(qb.to(dev), 2)
+    torch.cuda.synchronize()
+    inp = base
+    inp.q = codes.cpu().numpy()
+    inp.q_descale = s.cpu().numpy()
+    q, k, v, kw = tensors(inp)
+    out, lse = binding.prefill(q, k, v, return_lse=True, **kw)
+    torch.cuda.synchronize()
+    print(check_against_oracle(inp, out.float().cpu().numpy(), lse.cpu().numpy(), "quantized q prefill",
+                               tile_n=prefill_tile(128, 128)), flush=True)
