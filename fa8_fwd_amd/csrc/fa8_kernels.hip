@@ -382,10 +382,17 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
   const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
 
-  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order ----
+  // ---- per 64-key half pk: P of its keys (E4M3, PV-operand order), its row-sum MFMA and its
+  //      PV MFMAs, so that the MFMAs of one half overlap the exponentials of the next ----
+  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  const int trj = (lane & 15) >> 1;
+  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
+  const int tr_chunk_hi = (lane >> 4) & 1;
+  const int tr_byte = 8 * (lane & 1);
   v8i pop[PK];
+  v16f rs, ot[NB];
 #pragma unroll
-  for (int pk = 0; pk < PK; pk++)
+  for (int pk = 0; pk < PK; pk++) {
 #pragma unroll
     for (int w = 0; w < 8; w++) {
       const int kb = 2 * pk + (w >> 2), r0 = 4 * (w & 3);
@@ -397,30 +404,9 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pop[pk][w] = word;
     }
-  // ---- row sum of the rounded P on the MFMA: an all-ones A operand (E4M3 1.0 = 0x38) makes
-  //      every output row the sum over the keys of this lane's query row ----
-  {
-    const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
-    v16f rs;
+    rs = (pk == 0) ? mfma_32x32x64_fp8(ones, pop[0], (v16f){}) : mfma_32x32x64_fp8(ones, pop[pk], rs);
 #pragma unroll
-    for (int r = 0; r < 16; r++) rs[r] = 0.0f;
-#pragma unroll
-    for (int pk = 0; pk < PK; pk++) rs = mfma_32x32x64_fp8(ones, pop[pk], rs);
-    l_run = alpha * l_run + rs[0];
-  }
-
-  // ---- O_tile = V^T P^T from zero over this tile, then O = alpha * O + O_tile ----
-  const int trj = (lane & 15) >> 1;
-  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
-  const int tr_chunk_hi = (lane >> 4) & 1;
-  const int tr_byte = 8 * (lane & 1);
-#pragma unroll
-  for (int n = 0; n < NB; n++) {
-    v16f ot;
-#pragma unroll
-    for (int r = 0; r < 16; r++) ot[r] = 0.0f;
-#pragma unroll
-    for (int pk = 0; pk < PK; pk++) {
+    for (int n = 0; n < NB; n++) {
       v8i vop;
 #pragma unroll
       for (int r = 0; r < 4; r++) {
@@ -431,11 +417,15 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
         vop[2 * r] = x[0];
         vop[2 * r + 1] = x[1];
       }
-      ot = mfma_32x32x64_fp8(vop, pop[pk], ot);
+      ot[n] = (pk == 0) ? mfma_32x32x64_fp8(vop, pop[0], (v16f){}) : mfma_32x32x64_fp8(vop, pop[pk], ot[n]);
     }
-#pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[r]);
   }
+  l_run = alpha * l_run + rs[0];
+  // ---- O = alpha * O + O_tile ----
+#pragma unroll
+  for (int n = 0; n < NB; n++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[n][r]);
 }
 
 // One 64-key tile for decode, on the 16x16x128 FP8 MFMA: NQB blocks of 16 query rows (decode
