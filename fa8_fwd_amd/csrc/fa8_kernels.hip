@@ -382,15 +382,33 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
   const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
 
-  // ---- per 64-key half pk: P of its keys (E4M3, PV-operand order), its row-sum MFMA and its
-  //      PV MFMAs, so that the MFMAs of one half overlap the exponentials of the next ----
+  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order, its row sum on the MFMA (an all-ones
+  //      A operand, E4M3 1.0 = 0x38, makes every output row the sum over this lane's query row's
+  //      keys) and O_tile = V^T P^T from zero. At dv = 128 with two 64-key halves, each half's PV
+  //      MFMAs follow its own exponentials, so they overlap those of the next half (measured
+  //      faster there; slower at dv = 64 and 96, and at dv >= 192 the O_tile registers kept live
+  //      would spill). Otherwise O_tile goes column block by column block after all of P ----
+  constexpr bool kOverlap = PK > 1 && NB == 4;
   const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
   const int trj = (lane & 15) >> 1;
   const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
   const int tr_chunk_hi = (lane >> 4) & 1;
   const int tr_byte = 8 * (lane & 1);
+  auto v_operand = [&](int pk, int n) {
+    v8i vop;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int row = 64 * pk + 16 * r + tr_key;
+      const int ch = 2 * n + tr_chunk_hi;
+      const int off = row * DV + swz<VCH>(ch, v_sv(row)) * 16 + tr_byte;
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + off));
+      vop[2 * r] = x[0];
+      vop[2 * r + 1] = x[1];
+    }
+    return vop;
+  };
   v8i pop[PK];
-  v16f rs, ot[NB];
+  v16f rs, ot[kOverlap ? NB : 1];
 #pragma unroll
   for (int pk = 0; pk < PK; pk++) {
 #pragma unroll
@@ -405,27 +423,27 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       pop[pk][w] = word;
     }
     rs = (pk == 0) ? mfma_32x32x64_fp8(ones, pop[0], (v16f){}) : mfma_32x32x64_fp8(ones, pop[pk], rs);
+    if constexpr (kOverlap) {
 #pragma unroll
-    for (int n = 0; n < NB; n++) {
-      v8i vop;
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int row = 64 * pk + 16 * r + tr_key;
-        const int ch = 2 * n + tr_chunk_hi;
-        const int off = row * DV + swz<VCH>(ch, v_sv(row)) * 16 + tr_byte;
-        const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + off));
-        vop[2 * r] = x[0];
-        vop[2 * r + 1] = x[1];
+      for (int n = 0; n < NB; n++) {
+        const v8i vop = v_operand(pk, n);
+        ot[n] = (pk == 0) ? mfma_32x32x64_fp8(vop, pop[0], (v16f){}) : mfma_32x32x64_fp8(vop, pop[pk], ot[n]);
       }
-      ot[n] = (pk == 0) ? mfma_32x32x64_fp8(vop, pop[0], (v16f){}) : mfma_32x32x64_fp8(vop, pop[pk], ot[n]);
     }
   }
   l_run = alpha * l_run + rs[0];
   // ---- O = alpha * O + O_tile ----
 #pragma unroll
-  for (int n = 0; n < NB; n++)
+  for (int n = 0; n < NB; n++) {
+    if constexpr (!kOverlap) {
+      ot[0] = mfma_32x32x64_fp8(v_operand(0, n), pop[0], (v16f){});
 #pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[n][r]);
+      for (int pk = 1; pk < PK; pk++) ot[0] = mfma_32x32x64_fp8(v_operand(pk, n), pop[pk], ot[0]);
+    }
+    const v16f& t = ot[kOverlap ? n : 0];
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], t[r]);
+  }
 }
 
 // One 64-key tile for decode, on the 16x16x128 FP8 MFMA: NQB blocks of 16 query rows (decode
