@@ -945,8 +945,9 @@ fa8_decode_kernel(const KParams p) {
   // Loads of tile t into one register stage. A step past the window end (real == false)
   // issues the same loads, which then return zeros (or read the filler block): every step
   // issues the same loads, so the compiler's in-order wait counts are exact and each tile's
-  // wait leaves the DEPTH-1 younger tiles in flight.
-  auto gload = [&](int t, bool real, v4i (&ks)[KPT], v4i (&vs)[VPT]) {
+  // wait leaves the DEPTH-1 younger tiles in flight. (Forced inline: at d = 256 with the
+  // per-lane page lookup the compiler would otherwise make it a call with a stack frame.)
+  auto gload = [&](int t, bool real, v4i (&ks)[KPT], v4i (&vs)[VPT]) __attribute__((always_inline)) {
     const int j0 = t * BN;
 #pragma unroll
     for (int u = 0; u < KPT; u++) ks[u] = chunk_load(false, j0, u, real);

@@ -226,3 +226,20 @@ def test_quantize_q_host_validation():
     assert lib.fa8_quantize_q(ctypes.byref(p), None, None) == binding.FA8_OK
     p.batch = 3
     assert lib.fa8_quantize_q_workspace_bytes(ctypes.byref(p)) == 3 * 4 * 1 * 4   # 16 rows: one 32-row chunk
+
+
+def test_kernels_use_no_scratch():
+    """The last build recorded each kernel's registers and scratch: no template instance spills
+    in its loop or calls a helper with a stack frame, and the prefill and the decode kernels keep
+    the waves per SIMD their launch bounds ask for."""
+    from fa8_fwd_amd import build as B
+    if not os.path.exists(B.RESOURCES):
+        pytest.skip("library not built")
+    usage = __import__("json").load(open(B.RESOURCES))
+    assert usage, "no kernel resource remarks recorded"
+    for name, u in usage.items():
+        assert int(u["ScratchSize"]) <= B.MAX_SCRATCH_BYTES, (name, u)
+        assert u.get("Dynamic Stack") != "True", name
+        if "fa8_prefill_kernel" in name or "fa8_decode_heads_kernel" in name:
+            assert int(u["Occupancy"]) >= 2, (name, u)
+    assert any("fa8_prefill_kernel" in n for n in usage) and any("fa8_decode_kernel" in n for n in usage)
