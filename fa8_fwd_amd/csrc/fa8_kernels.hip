@@ -179,23 +179,22 @@ __device__ __forceinline__ int cvt_pk_fp8_lo(float a, float b) {
   __asm__("v_cvt_pk_fp8_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
-// max of three floats as one v_max3_f32 (fmaxf would first quiet each MFMA result with an extra
-// v_max_f32 x, x, which IEEE mode requires of maxnum)
+// max of three floats as one v_maximum3_f32 (IEEE 754-2019 maximum, which needs no quieting of
+// its inputs: fmaxf would first quiet each MFMA result with an extra v_max_f32 x, x). A builtin
+// rather than inline assembly, so the compiler knows the instruction and schedules it freely.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 // Cross-lane moves within a wave through the gfx950 permlane swaps (VALU, no LDS round trip).
 // permlane16_swap(x, x) leaves {x of row 2k, x of row 2k+1} in both rows of each pair of
 // 16-lane rows, permlane32_swap(x, x) leaves {x of rows 0-1, x of rows 2-3} in both halves.
 __device__ __forceinline__ float max_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -368,11 +367,13 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
 
   // ---- row max (lanes L and L^32 share a row), lazy rescale ----
-  float mx = kNegInf;
+  // four independent chains, so consecutive max instructions do not wait on each other
+  float mxc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
   for (int kb = 0; kb < KB; kb++)
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = max3f(mx, sacc[kb][r], sacc[kb][r + 1]);
+    for (int r = 0; r < 16; r += 2) mxc[(r >> 1) & 3] = max3f(mxc[(r >> 1) & 3], sacc[kb][r], sacc[kb][r + 1]);
+  float mx = max3f(mxc[0], mxc[1], __builtin_elementwise_maximum(mxc[2], mxc[3]));
   mx = max_xor32(mx);
   const float mt = mx * c;
   float alpha = 1.0f;
@@ -422,7 +423,6 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pop[pk][w] = word;
     }
-    rs = (pk == 0) ? mfma_32x32x64_fp8(ones, pop[0], (v16f){}) : mfma_32x32x64_fp8(ones, pop[pk], rs);
     if constexpr (kOverlap) {
 #pragma unroll
       for (int n = 0; n < NB; n++) {
@@ -430,6 +430,8 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
         ot[n] = (pk == 0) ? mfma_32x32x64_fp8(vop, pop[0], (v16f){}) : mfma_32x32x64_fp8(vop, pop[pk], ot[n]);
       }
     }
+    // the row sum after the PV MFMAs of the half: its result is read last
+    rs = (pk == 0) ? mfma_32x32x64_fp8(ones, pop[0], (v16f){}) : mfma_32x32x64_fp8(ones, pop[pk], rs);
   }
   l_run = alpha * l_run + rs[0];
   // ---- O = alpha * O + O_tile ----
