@@ -53,6 +53,11 @@ class AttnInputs:
     out_dtype: str = "bf16"                     # "bf16" | "fp16"
     name: str = ""
     sink: Optional[np.ndarray] = None           # float32 [Hq] learnable sink logits, or None
+    # MXFP8 block scales (E8M0 bytes), dense layouts: Q [B, Sq, Hq, d/32] and K [B, Sk, Hkv,
+    # d/32] per 32 elements of d; V [B, ceil(Sk/32), Hkv, dv] per 32 keys
+    q_mx: Optional[np.ndarray] = None
+    k_mx: Optional[np.ndarray] = None
+    v_mx: Optional[np.ndarray] = None
 
     # --- per-batch lengths, resolved from whichever layout is in use ---
     def seqlens_q(self) -> np.ndarray:
@@ -183,6 +188,23 @@ def with_sink(inp: AttnInputs, seed: int, mean: float = 0.0, std: float = 1.0) -
     g = torch.Generator().manual_seed(seed)
     z = torch.randn((inp.heads_q,), generator=g, dtype=torch.float32) * std + mean
     return dataclasses.replace(inp, sink=z.numpy().astype(np.float32), name=inp.name + "_sink")
+
+
+def with_mx(inp: AttnInputs, seed: int, lo: int = 122, hi: int = 132) -> AttnInputs:
+    """A copy of a dense input with MXFP8 block scales: E8M0 bytes uniform in [lo, hi] (scales
+    2^(lo-127) .. 2^(hi-127)), drawn Q, K, V in that order from their own seeded generator; the
+    E4M3 elements are the input's own. The per-tensor descales are dropped (the block scales
+    take their place)."""
+    if inp.cu_seqlens_q is not None or inp.cu_seqlens_k is not None or inp.block_table is not None:
+        raise ValueError("MX scales are generated for dense layouts")
+    g = torch.Generator().manual_seed(seed)
+    B, Sq, Sk = inp.batch, inp.max_seqlen_q, inp.max_seqlen_k
+    qs = torch.randint(lo, hi + 1, (B, Sq, inp.heads_q, inp.d // 32), generator=g, dtype=torch.int32)
+    ks = torch.randint(lo, hi + 1, (B, Sk, inp.heads_kv, inp.d // 32), generator=g, dtype=torch.int32)
+    vs = torch.randint(lo, hi + 1, (B, (Sk + 31) // 32, inp.heads_kv, inp.dv), generator=g, dtype=torch.int32)
+    return dataclasses.replace(inp, q_mx=qs.numpy().astype(np.uint8), k_mx=ks.numpy().astype(np.uint8),
+                               v_mx=vs.numpy().astype(np.uint8), q_descale=None, k_descale=None,
+                               v_descale=None, name=inp.name + "_mx")
 
 
 def random_lengths(gen: torch.Generator, n: int, lo: int, hi: int) -> np.ndarray:

@@ -12,6 +12,10 @@ import this package. It never imports the HIP package and shares no code with it
 * ``combine``: the log-sum-exp merge of split partial results (the split-KV combine that the
   same page times inside each decode step), written out in fp64.
 * ``e4m3_table``: the oracle's own E4M3FN decode table (OCP definition).
+* MXFP8 inputs: when the input carries E8M0 block scales (``q_mx``, ``k_mx``, ``v_mx``),
+  ``attention`` dequantizes each 32-element block along the contraction dimension with its
+  scale before the same fp64 definition (FlashAttention-4 MXFP8 page, sections 1 and 2.1; E8M0
+  from the OCP Microscaling Formats specification).
 
 The emulator of the method's own steps (tiles, lazy rescale, biased FP8 P) is in
 ``oracle.emulator``; it is a diagnostic, not the parity reference.
@@ -56,6 +60,9 @@ class _Params(ctypes.Structure):
         ("softmax_scale", ctypes.c_double),
         ("causal", ctypes.c_int32), ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
         ("sink", ctypes.c_void_p),
+        ("q_mx", ctypes.c_void_p), ("qmx_ss", ctypes.c_int64), ("qmx_sh", ctypes.c_int64), ("qmx_base", ctypes.c_void_p),
+        ("k_mx", ctypes.c_void_p), ("kmx_ss", ctypes.c_int64), ("kmx_sh", ctypes.c_int64), ("kmx_base", ctypes.c_void_p),
+        ("v_mx", ctypes.c_void_p), ("vmx_sb", ctypes.c_int64), ("vmx_sh", ctypes.c_int64), ("vmx_base", ctypes.c_void_p),
     ]
 
 
@@ -190,6 +197,40 @@ def attention(inp, rows=None, key_range=None, threads: Optional[int] = None, sof
             raise ValueError("sink must hold one logit per query head")
         keep.append(z)
     p.sink = _ptr(z)
+    # MXFP8 block scales (E8M0 bytes), when the input carries them: Q [.., Hq, d/32] per query
+    # row, K [.., Hkv, d/32] per key row, V [B, ceil(Sk/32), Hkv, dv] per 32-key block (dense
+    # K/V only)
+    q_mx, k_mx, v_mx = (getattr(inp, f, None) for f in ("q_mx", "k_mx", "v_mx"))
+    if q_mx is not None or k_mx is not None or v_mx is not None:
+        if inp.block_table is not None:
+            raise ValueError("MX scales need non-paged K/V")
+        nq, nk = d // 32, d // 32
+        if q_mx is not None:
+            q_mx = np.ascontiguousarray(np.asarray(q_mx, np.uint8))
+            if inp.cu_seqlens_q is not None:
+                qb = np.asarray(inp.cu_seqlens_q[:-1], np.int64) * (Hq * nq)
+            else:
+                qb = np.arange(B, dtype=np.int64) * (inp.max_seqlen_q * Hq * nq)
+            qb = np.ascontiguousarray(qb)
+            keep += [q_mx, qb]
+            p.q_mx, p.qmx_ss, p.qmx_sh, p.qmx_base = q_mx.ctypes.data, Hq * nq, nq, qb.ctypes.data
+        if k_mx is not None:
+            k_mx = np.ascontiguousarray(np.asarray(k_mx, np.uint8))
+            if inp.cu_seqlens_k is not None:
+                kb2 = np.asarray(inp.cu_seqlens_k[:-1], np.int64) * (Hkv * nk)
+            else:
+                kb2 = np.arange(B, dtype=np.int64) * (inp.max_seqlen_k * Hkv * nk)
+            kb2 = np.ascontiguousarray(kb2)
+            keep += [k_mx, kb2]
+            p.k_mx, p.kmx_ss, p.kmx_sh, p.kmx_base = k_mx.ctypes.data, Hkv * nk, nk, kb2.ctypes.data
+        if v_mx is not None:
+            if inp.cu_seqlens_k is not None or inp.seqused_k is not None:
+                raise ValueError("V block scales need the dense K/V layout")
+            v_mx = np.ascontiguousarray(np.asarray(v_mx, np.uint8))
+            nblk = (inp.max_seqlen_k + 31) // 32
+            vb = np.ascontiguousarray(np.arange(B, dtype=np.int64) * (nblk * Hkv * dv))
+            keep += [v_mx, vb]
+            p.v_mx, p.vmx_sb, p.vmx_sh, p.vmx_base = v_mx.ctypes.data, Hkv * dv, dv, vb.ctypes.data
     klo = khi = None
     if key_range is not None:
         klo = np.ascontiguousarray(np.asarray(key_range[0], np.int64))

@@ -30,6 +30,16 @@
  *     O     = dv[b,kvh] * sum_J w_j v_j / l,    LSE = m + ln l
  *     J empty  ->  O = 0, LSE = z_h
  *
+ *   with MXFP8 block scales (the MXFP8 forward of the FlashAttention-4 MXFP8 page, sections 1
+ *   and 2.1: E4M3 elements with one E8M0 scale per 32 elements along each product's
+ *   contraction dimension, i.e. along d for Q and K and along the keys for V; E8M0 as defined
+ *   by the OCP Microscaling Formats specification: an unsigned 8-bit exponent with bias 127,
+ *   value 2^(e - 127), 0xFF = NaN):
+ *     q_c   = E4M3(q8_c) * 2^(qs[c / 32] - 127)     per query row
+ *     k_j,c = E4M3(k8_j,c) * 2^(ks_j[c / 32] - 127) per key row
+ *     v_j,c = E4M3(v8_j,c) * 2^(vs[j / 32][c] - 127)   key blocks counted from the sequence start
+ *   and otherwise the same definition (descales, when also given, still multiply).
+ *
  * Note: every E4M3 value is an integer multiple of 2^-9 with magnitude <= 448 = 229376*2^-9,
  * so each product q_c*k_c is an integer multiple of 2^-18 below 2^36 * 2^-18 and any sum of up
  * to 256 of them stays below 2^44 * 2^-18: the dot product is exact in fp64 whatever the order.
@@ -89,7 +99,26 @@ typedef struct {
   double softmax_scale;
   int32_t causal, window_left, window_right;
   const double* sink;          /* [Hq] sink logits, or NULL (no sink) */
+  /* MXFP8 block scales (E8M0 bytes), each NULL when absent; non-paged layouts only.
+   * Q: [.., d/32] per query row at q_mx + qmx_base[b] + i*qmx_ss + h*qmx_sh;
+   * K: [.., d/32] per key row at k_mx + kmx_base[b] + j*kmx_ss + kvh*kmx_sh;
+   * V: [.., dv] per 32-key block at v_mx + vmx_base[b] + (j/32)*vmx_sb + kvh*vmx_sh. */
+  const uint8_t* q_mx;
+  int64_t qmx_ss, qmx_sh;
+  const int64_t* qmx_base;
+  const uint8_t* k_mx;
+  int64_t kmx_ss, kmx_sh;
+  const int64_t* kmx_base;
+  const uint8_t* v_mx;
+  int64_t vmx_sb, vmx_sh;
+  const int64_t* vmx_base;
 } fa8_oracle_params;
+
+/* E8M0 scale byte (OCP Microscaling Formats): 2^(e - 127); 0xFF encodes NaN. */
+static double e8m0_value(unsigned e) {
+  if (e == 255u) return NAN;
+  return ldexp(1.0, (int)e - 127);
+}
 
 static int64_t key_offset(const fa8_oracle_params* p, int b, int64_t j, int kvh, int is_v) {
   int64_t ss = is_v ? p->v_ss : p->k_ss, sh = is_v ? p->v_sh : p->k_sh;
@@ -127,12 +156,17 @@ static void one_row(const fa8_oracle_params* p, int b, int h, int i, int64_t klo
   const uint8_t* qrow = p->q + p->q_base[b] + (int64_t)i * p->q_ss + (int64_t)h * p->q_sh;
   double qv[512];
   for (int c = 0; c < p->d; c++) qv[c] = g_table[qrow[c]];
+  if (p->q_mx) {
+    const uint8_t* qs = p->q_mx + p->qmx_base[b] + (int64_t)i * p->qmx_ss + (int64_t)h * p->qmx_sh;
+    for (int c = 0; c < p->d; c++) qv[c] *= e8m0_value(qs[c / 32]);
+  }
 
   double m = -INFINITY;
   for (int64_t j = lo; j < hi; j++) {
     const uint8_t* krow = p->k + key_offset(p, b, j, kvh, 0);
+    const uint8_t* ks = p->k_mx ? p->k_mx + p->kmx_base[b] + j * p->kmx_ss + (int64_t)kvh * p->kmx_sh : NULL;
     double r = 0.0;
-    for (int c = 0; c < p->d; c++) r += qv[c] * g_table[krow[c]];
+    for (int c = 0; c < p->d; c++) r += qv[c] * (ks ? g_table[krow[c]] * e8m0_value(ks[c / 32]) : g_table[krow[c]]);
     double s = sigma * r;
     scores[j - lo] = s;
     if (s > m) m = s;
@@ -143,7 +177,8 @@ static void one_row(const fa8_oracle_params* p, int b, int h, int i, int64_t klo
     double w = exp(scores[j - lo] - m);
     l += w;
     const uint8_t* vrow = p->v + key_offset(p, b, j, kvh, 1);
-    for (int c = 0; c < p->dv; c++) out[c] += w * g_table[vrow[c]];
+    const uint8_t* vs = p->v_mx ? p->v_mx + p->vmx_base[b] + (j / 32) * p->vmx_sb + (int64_t)kvh * p->vmx_sh : NULL;
+    for (int c = 0; c < p->dv; c++) out[c] += w * (vs ? g_table[vrow[c]] * e8m0_value(vs[c]) : g_table[vrow[c]]);
   }
   for (int c = 0; c < p->dv; c++) out[c] = dv * out[c] / l;
   *lse = m + log(l);
@@ -158,6 +193,8 @@ int fa8_oracle_attention(const fa8_oracle_params* p, int64_t n, const int32_t* r
   if (!p || p->heads_kv <= 0 || p->heads_q % p->heads_kv != 0 || p->d > 512 || p->d <= 0 || p->dv <= 0)
     return -1;
   if (p->block_table && p->page_size <= 0) return -1;
+  if (p->block_table && (p->q_mx || p->k_mx || p->v_mx)) return -1;
+  if ((p->q_mx && !p->qmx_base) || (p->k_mx && !p->kmx_base) || (p->v_mx && !p->vmx_base)) return -1;
   build_table();
   int64_t maxk = 1;
   for (int b = 0; b < p->batch; b++)
