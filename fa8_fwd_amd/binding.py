@@ -61,6 +61,15 @@ class FwdParams(ctypes.Structure):
 _lib = None
 
 
+class MXScales(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_batch_stride", ctypes.c_int64), ("q_row_stride", ctypes.c_int64),
+                ("q_head_stride", ctypes.c_int64),
+                ("k", ctypes.c_void_p), ("k_batch_stride", ctypes.c_int64), ("k_row_stride", ctypes.c_int64),
+                ("k_head_stride", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("v_batch_stride", ctypes.c_int64), ("v_block_stride", ctypes.c_int64),
+                ("v_head_stride", ctypes.c_int64)]
+
+
 def lib_path() -> str:
     return _LIB_PATH
 
@@ -91,6 +100,7 @@ def load():
     P = ctypes.POINTER(FwdParams)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.fa8_fwd_prefill.argtypes = [P, vp]
+    lib.fa8_fwd_prefill_mx.argtypes = [P, ctypes.POINTER(MXScales), vp]
     lib.fa8_fwd_decode_splitkv.argtypes = [P, i32, vp, vp, vp]
     lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, vp]
     lib.fa8_check_params.argtypes = [P, i32]
@@ -99,7 +109,7 @@ def load():
     lib.fa8_quantize_q_workspace_bytes.restype = ctypes.c_int64
     lib.fa8_quantize_q.argtypes = [QP, vp, vp]
     lib.fa8_quantize_q.restype = ctypes.c_int
-    for f in ("fa8_fwd_prefill", "fa8_fwd_decode_splitkv", "fa8_combine", "fa8_check_params"):
+    for f in ("fa8_fwd_prefill", "fa8_fwd_prefill_mx", "fa8_fwd_decode_splitkv", "fa8_combine", "fa8_check_params"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fa8_decode_num_splits.argtypes = [i32, i32, i32, i32]
     lib.fa8_decode_num_splits.restype = i32
@@ -285,6 +295,40 @@ def prefill(q, k, v, *, cu_seqlens_q=None, cu_seqlens_k=None, seqused_k=None, bl
     _set_out(p, out, lse, varlen_q)
     p.sink = _sink_ptr(sink, p.heads_q)
     _check(lib.fa8_fwd_prefill(ctypes.byref(p), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def _scale_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must hold E8M0 scale bytes (torch.uint8), got {t.dtype}")
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be 4-D with a contiguous last dimension")
+    return t
+
+
+def prefill_mx(q, k, v, q_scale, k_scale, v_scale, *, softmax_scale: float = 0.0, causal: bool = False,
+               window_left: int = -1, window_right: int = -1, out: Optional[torch.Tensor] = None,
+               out_dtype=torch.bfloat16, return_lse: bool = False, lse: Optional[torch.Tensor] = None,
+               sink: Optional[torch.Tensor] = None, stream=None):
+    """MXFP8 attention forward (fa8_fwd_prefill_mx). q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] E4M3;
+    q_scale [B, Sq, Hq, d/32], k_scale [B, Sk, Hkv, d/32], v_scale [B, ceil(Sk/32), Hkv, dv] E8M0
+    bytes (uint8). Returns out, or (out, lse)."""
+    lib = load()
+    p = _params(q, k, v, None, None, None, None, None, None, None, None, None, softmax_scale, causal,
+                window_left, window_right)
+    if out is None:
+        out, lse2 = _alloc_out(q, p.dv, out_dtype, False, return_lse and lse is None, p.batch, p.heads_q,
+                               p.max_seqlen_q)
+        lse = lse if lse is not None else lse2
+    elif return_lse and lse is None:
+        _, lse = _alloc_out(q, p.dv, out.dtype, False, True, p.batch, p.heads_q, p.max_seqlen_q)
+    _set_out(p, out, lse, False)
+    p.sink = _sink_ptr(sink, p.heads_q)
+    qs, ks, vs = _scale_bytes(q_scale, "q_scale"), _scale_bytes(k_scale, "k_scale"), _scale_bytes(v_scale, "v_scale")
+    m = MXScales(qs.data_ptr(), qs.stride(0), qs.stride(1), qs.stride(2),
+                 ks.data_ptr(), ks.stride(0), ks.stride(1), ks.stride(2),
+                 vs.data_ptr(), vs.stride(0), vs.stride(1), vs.stride(2))
+    _check(lib.fa8_fwd_prefill_mx(ctypes.byref(p), ctypes.byref(m), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

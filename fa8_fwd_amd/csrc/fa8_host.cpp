@@ -299,6 +299,41 @@ fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream) {
   return ok();
 }
 
+fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, void* stream) {
+  if (!s) return fail(FA8_ERR_INVALID, "MX scales must be non-NULL");
+  fa8_status st = validate(p, 0);
+  if (st != FA8_OK) return st;
+  if (!((p->d == 64 && p->dv == 64) || (p->d == 128 && p->dv == 128)))
+    return fail(FA8_ERR_UNSUPPORTED, "MX prefill supports (d, dv) = (64, 64) or (128, 128), not (%d, %d)", p->d, p->dv);
+  if (p->cu_seqlens_q || p->cu_seqlens_k || p->seqused_k || p->block_table)
+    return fail(FA8_ERR_UNSUPPORTED, "MX prefill takes fixed-length Q and K/V only");
+  if (p->q_descale.ptr || p->k_descale.ptr || p->v_descale.ptr)
+    return fail(FA8_ERR_INVALID, "MX prefill takes no descales (the block scales replace them)");
+  if (!s->q || !s->k || !s->v) return fail(FA8_ERR_INVALID, "MX scale pointers must be non-NULL");
+  const int64_t nb = p->d / 32;
+  auto mult = [](int64_t x, int64_t m) { return x % m == 0; };
+  if (!mult((int64_t)(uintptr_t)s->q, nb) || !mult(s->q_batch_stride, nb) || !mult(s->q_row_stride, nb) ||
+      !mult(s->q_head_stride, nb) || !mult((int64_t)(uintptr_t)s->k, nb) || !mult(s->k_batch_stride, nb) ||
+      !mult(s->k_row_stride, nb) || !mult(s->k_head_stride, nb))
+    return fail(FA8_ERR_INVALID, "Q/K scale pointers and strides must be multiples of d/32 = %d", (int)nb);
+  if (!mult((int64_t)(uintptr_t)s->v, 16) || !mult(s->v_batch_stride, 16) || !mult(s->v_block_stride, 16) ||
+      !mult(s->v_head_stride, 16))
+    return fail(FA8_ERR_INVALID, "V scale pointer and strides must be multiples of 16");
+  if (s->q_batch_stride < 0 || s->q_row_stride < 0 || s->q_head_stride < 0 || s->k_batch_stride < 0 ||
+      s->k_row_stride < 0 || s->k_head_stride < 0 || s->v_batch_stride < 0 || s->v_block_stride < 0 ||
+      s->v_head_stride < 0)
+    return fail(FA8_ERR_INVALID, "MX scale strides must be non-negative");
+  if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
+  fa8::KParams k = make_kparams(p);
+  k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
+  k.q_mx = s->q; k.qmx_bs = s->q_batch_stride; k.qmx_rs = s->q_row_stride; k.qmx_hs = s->q_head_stride;
+  k.k_mx = s->k; k.kmx_bs = s->k_batch_stride; k.kmx_rs = s->k_row_stride; k.kmx_hs = s->k_head_stride;
+  k.v_mx = s->v; k.vmx_bs = s->v_batch_stride; k.vmx_ts = s->v_block_stride; k.vmx_hs = s->v_head_stride;
+  hipError_t e = fa8::launch_prefill_mx(k, p->d, p->dv, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA8_ERR_HIP, "MX prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, float* o_partial, float* lse_partial,
                                   void* stream) {
   if (num_splits < 1) return fail(FA8_ERR_INVALID, "num_splits must be >= 1 (got %d)", num_splits);

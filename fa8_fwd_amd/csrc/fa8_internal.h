@@ -31,6 +31,10 @@ struct KParams {
   float* o_part; float* lse_part; int32_t nsplit;
   int32_t nmb;                // row blocks per (batch, head) (decode) or per (batch, q head) (prefill)
   const float* sink;          // [hq] sink logits or null (prefill finalize only)
+  // MXFP8 block scales (E8M0 bytes; strides in bytes), MX prefill only
+  const uint8_t* q_mx; int64_t qmx_bs, qmx_rs, qmx_hs;
+  const uint8_t* k_mx; int64_t kmx_bs, kmx_rs, kmx_hs;
+  const uint8_t* v_mx; int64_t vmx_bs, vmx_ts, vmx_hs;   // vmx_ts: per 32-key block
 };
 
 struct CParams {
@@ -66,6 +70,7 @@ int decode_heads_choice(const KParams& kp, int d, int dv);
 int decode_units_per_split(const KParams& kp, int d, int dv);
 
 hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream);
+hipError_t launch_prefill_mx(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_combine(const CParams& cp, hipStream_t stream);
 

@@ -50,6 +50,7 @@ constexpr float kTau = 0.75f;    // lazy-rescale slack in log2 units, <= log2(44
 constexpr float kBias = 8.0f;    // P is computed as 2^(x - m + 8)
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLog2E4M3Max = 8.80735492205760410f;   // log2(448), E4M3's largest finite value
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // 1 KB read by the decode kernel's pipeline-filler loads (one 16-byte chunk per lane): a small
@@ -317,6 +318,29 @@ __device__ __forceinline__ void load_q(const uint8_t* qrow, bool valid, int hgrp
   }
 }
 
+// A operand (V^T) of the PV MFMA for k-step pk (keys 64 pk ..) and output column block n, in
+// the key order of the S^T accumulator (the order attn_tile uses).
+template <int DV>
+__device__ __forceinline__ v8i pv_operand_mx(const FA8_LDS uint8_t* vt, int pk, int n, int lane) {
+  constexpr int VCH = DV / 16;
+  const int hgrp = lane >> 5;
+  const int trj = (lane & 15) >> 1;
+  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
+  const int tr_chunk_hi = (lane >> 4) & 1;
+  const int tr_byte = 8 * (lane & 1);
+  v8i vop;
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int row = 64 * pk + 16 * r + tr_key;
+    const int ch = 2 * n + tr_chunk_hi;
+    const int off = row * DV + swz<VCH>(ch, v_sv(row)) * 16 + tr_byte;
+    const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + off));
+    vop[2 * r] = x[0];
+    vop[2 * r + 1] = x[1];
+  }
+  return vop;
+}
+
 // One KV tile of BN keys (LDS K tile at kt, V tile at vt, both row-major and swizzled) for the
 // 32 query rows of this wave. Updates the running max m, row sum l and O accumulators.
 template <int D, int DV, int BN>
@@ -554,26 +578,28 @@ __device__ __forceinline__ void attn_tile16(const FA8_LDS uint8_t* kt, const FA8
   }
 }
 
-// Final normalization and store of one lane's row (or its partial for split-KV decode).
-// Without SPLIT, a learnable sink logit z (p.sink) joins the row sum here with the same 2^8
+// Final normalization and store of one lane's row (or its partial for split-KV decode). bias
+// is P's exponent offset (8 for E4M3 P, 0 for MXFP8 P, whose block scales carry the range).
+// Without SPLIT, a learnable sink logit z (p.sink) joins the row sum here with the same
 // offset as P: the stored max m rises to z2 = z log2 e when z2 is larger (alpha = 2^(m - m')
 // rescales l and O; every term stays below 2^8), then l += 2^(z2 - m' + 8). Split partials
 // leave the sink to the combine.
 template <int DV, bool SPLIT>
 __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[DV / 32], float m_run, float l_tot,
-                                          float dvs, int hgrp, int b, int q0, int qi, int qh, int split) {
+                                          float dvs, int hgrp, int b, int q0, int qi, int qh, int split,
+                                          float bias = kBias) {
   constexpr int NB = DV / 32;
   const float z2 = (!SPLIT && p.sink) ? p.sink[qh] * kLog2e : kNegInf;
   if (z2 != kNegInf) {
     const float mf = fmaxf(m_run, z2);
     const float a = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - mf);
-    l_tot = a * l_tot + fast_exp2(z2 - mf + kBias);
+    l_tot = a * l_tot + fast_exp2(z2 - mf + bias);
     dvs *= a;
     m_run = mf;
   }
   const bool nonempty = l_tot > 0.0f;
   const float inv = nonempty ? dvs / l_tot : 0.0f;
-  const float lse = nonempty ? (m_run + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
+  const float lse = nonempty ? (m_run + __log2f(l_tot) - bias) * kLn2 : kNegInf;
   if constexpr (SPLIT) {
     const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi) * p.hq + qh;
     float* orow = p.o_part + prow * DV;
@@ -757,6 +783,336 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   const float l_tot = l_run;   // the MFMA row sums already cover both lanes of a row
   if (!valid) return;
   store_row<DV, false>(p, oacc, m_run, l_tot, dvs, hgrp, b, si.q0, qi, qh, 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// MXFP8 forward pass (the MXFP8 forward of the FlashAttention-4 MXFP8 page, sections 2.1 and
+// 2.1.3). The structure of fa8_prefill_kernel; both products run on the block-scaled MFMA,
+// which applies one E8M0 scale per lane to the 32 contraction elements that scale covers.
+// Measured lane layout of v_mfma_scale_f32_32x32x64_f8f6f4: the scale byte of lane L scales
+// hardware k-block L/32 of row (A) or column (B) L%32, and k-block t is dwords 4t..4t+3 of BOTH
+// lanes of that row (L%32 and L%32+32). So:
+//  * Q and K (blocks of 32 along d): lane half h loads d-chunks 4ks+h and 4ks+2+h (16 bytes
+//    each) of k-step ks, which puts d [64ks, 64ks+32) in k-block 0 and [64ks+32, 64ks+64) in
+//    k-block 1, and supplies the scale of d-block 2ks+h;
+//  * P and V (blocks of 32 keys): the S^T accumulator order already puts keys [64pk, 64pk+32)
+//    of a 64-key step in dwords 0-3 of both lane halves and keys [64pk+32, 64pk+64) in dwords
+//    4-7 (and the transposed V reads follow the same key order), so lane half h supplies the
+//    scales of key block 2pk+h.
+// Per query row and 32-key block, the block's max x_b (log2 units) gives the shared exponent
+// X = ceil(x_b - m - log2 448) (m the running max), the smallest power of two that brings the
+// block's largest P = 2^(x_b - m) to at most 448, clamped to [-127, 127]; P = 2^(x - m - X) is
+// rounded to E4M3 with scale byte X + 127 (a min with 448 guards against exp2 rounding). Each
+// block's max comes from the row max's own reduction (two lanes hold a block's 32 keys), so no
+// extra pass over P is needed.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ v16f mfma_32x32x64_mx(v8i a, v8i b, v16f c, int sa, int sb) {
+  // E4M3 operands; opsel 0 takes each lane's scale from byte 0 of sa / sb
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Q row of this lane as the B operand in the block-scaled order: k-step ks takes d-chunks
+// 4ks+h and 4ks+2+h (h = lane half).
+template <int D>
+__device__ __forceinline__ void load_q_mx(const uint8_t* qrow, bool valid, int hgrp, v8i (&qop)[D / 64]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 64; ks++) {
+    v4i a = {0, 0, 0, 0}, a2 = {0, 0, 0, 0};
+    if (valid) {
+      a = ld_global16(qrow + (4 * ks + hgrp) * 16);
+      a2 = ld_global16(qrow + (4 * ks + 2 + hgrp) * 16);
+    }
+    qop[ks] = (v8i){a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+  }
+}
+
+// One BN-key tile with MXFP8 operands. kt/vt: K and V tiles (row-major, swizzled); ksc: the
+// tile's K scales [BN][D/32]; vsc: its V scales [BN/32][DV]; qsc: this lane's Q scale bytes
+// (d-block 2ks + h for k-step ks).
+template <int D, int DV, int BN>
+__device__ __forceinline__ void attn_tile_mx(const FA8_LDS uint8_t* kt, const FA8_LDS uint8_t* vt,
+                                             const FA8_LDS uint8_t* ksc, const FA8_LDS uint8_t* vsc,
+                                             const v8i (&qop)[D / 64], const int (&qsc)[D / 64], float c,
+                                             bool need_mask, int j0, int my_lo, int my_hi, int lane, float& m_run,
+                                             float& l_run, v16f (&oacc)[DV / 32]) {
+  constexpr int KB = BN / 32, PK = BN / 64, KS = D / 64, NB = DV / 32, KCH = D / 16, NBD = D / 32;
+  const int hgrp = lane >> 5, lrow = lane & 31;
+
+  // ---- S^T = K Q^T, each k-step scaled by the K and Q block scales ----
+  v16f sacc[KB];
+  const FA8_LDS uint8_t* ksc_lane = ksc + lrow * NBD;             // key row lrow of block 0
+#pragma unroll
+  for (int kb = 0; kb < KB; kb++) {
+    const int row = kb * 32 + lrow;
+    // this key row's D/32 scale bytes
+    const uint32_t kw = (NBD == 4) ? *(const FA8_LDS uint32_t*)(ksc_lane + kb * 32 * NBD)
+                                   : (uint32_t)*(const FA8_LDS uint16_t*)(ksc_lane + kb * 32 * NBD);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const v4i a = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(4 * ks + hgrp, k_sv<D>(row)) * 16);
+      const v4i a2 = *(const FA8_LDS v4i*)(kt + row * D + swz<KCH>(4 * ks + 2 + hgrp, k_sv<D>(row)) * 16);
+      const v8i kop = {a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+      const int sa = (int)((kw >> (8 * (2 * ks + hgrp))) & 0xffu);
+      sacc[kb] = (ks == 0) ? mfma_32x32x64_mx(kop, qop[0], (v16f){}, sa, qsc[0])
+                           : mfma_32x32x64_mx(kop, qop[ks], sacc[kb], sa, qsc[ks]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // bounds how far the K operand reads run ahead
+  }
+
+  // ---- mask ----
+  if (need_mask) {
+    const uint32_t span = (uint32_t)max(my_hi - my_lo, 0);
+    const int base = j0 + 4 * hgrp - my_lo;
+#pragma unroll
+    for (int kb = 0; kb < KB; kb++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const uint32_t rel = (uint32_t)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+        if (rel >= span) sacc[kb][r] = kNegInf;
+      }
+  }
+
+  // ---- per 32-key block max (two lanes hold a block's keys), row max, lazy rescale ----
+  float bmax[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; kb++) {
+    float m0 = max3f(sacc[kb][0], sacc[kb][1], sacc[kb][2]);
+    float m1 = max3f(sacc[kb][3], sacc[kb][4], sacc[kb][5]);
+    m0 = max3f(m0, sacc[kb][6], sacc[kb][7]);
+    m1 = max3f(m1, sacc[kb][8], sacc[kb][9]);
+    m0 = max3f(m0, sacc[kb][10], sacc[kb][11]);
+    m1 = max3f(m1, sacc[kb][12], sacc[kb][13]);
+    m0 = max3f(m0, sacc[kb][14], sacc[kb][15]);
+    bmax[kb] = max_xor32(__builtin_elementwise_maximum(m0, m1));
+  }
+  float mx = bmax[0];
+#pragma unroll
+  for (int kb = 1; kb < KB; kb++) mx = __builtin_elementwise_maximum(mx, bmax[kb]);
+  const float mt = mx * c;
+  float alpha = 1.0f;
+  if (mt - m_run > kTau) {
+    alpha = fast_exp2(m_run - mt);
+    m_run = mt;
+  }
+
+  // ---- P per 32-key block: shared exponent X, E4M3(2^(x - m - X)), scale X + 127 ----
+  int pscale[KB];
+  float nbk[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; kb++) {
+    const float y = bmax[kb] * c - m_run;                   // -inf for an all-masked block
+    const float xe = (m_run == kNegInf) ? -127.0f : fmaxf(ceilf(y - kLog2E4M3Max), -127.0f);
+    pscale[kb] = (int)xe + 127;
+    nbk[kb] = (m_run == kNegInf) ? 0.0f : -(m_run + xe);
+  }
+  v8i pop[PK];
+  int psc[PK];
+#pragma unroll
+  for (int pk = 0; pk < PK; pk++) {
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+      const int kb = 2 * pk + (w >> 2), r0 = 4 * (w & 3);
+      const float p0 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 0], c, nbk[kb])), 448.0f);
+      const float p1 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 1], c, nbk[kb])), 448.0f);
+      const float p2 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 2], c, nbk[kb])), 448.0f);
+      const float p3 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nbk[kb])), 448.0f);
+      int word = cvt_pk_fp8_lo(p0, p1);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
+      pop[pk][w] = word;
+    }
+    psc[pk] = hgrp ? pscale[2 * pk + 1] : pscale[2 * pk];   // this lane half's key block
+  }
+
+  // ---- row sum of the stored P times its scales, on the block-scaled MFMA ----
+  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  v16f rs = mfma_32x32x64_mx(ones, pop[0], (v16f){}, 127, psc[0]);
+#pragma unroll
+  for (int pk = 1; pk < PK; pk++) rs = mfma_32x32x64_mx(ones, pop[pk], rs, 127, psc[pk]);
+  l_run = alpha * l_run + rs[0];
+
+  // ---- O_tile = V^T P^T from zero per column block (V block scale x P block scale), then
+  //      O = alpha O + O_tile ----
+  const FA8_LDS uint8_t* vsc_lane = vsc + hgrp * DV + lrow;        // block hgrp, column lrow
+  // (scheduling barriers: without them the compiler reads every V operand of the tile during
+  // the exponentials and runs out of registers)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int n = 0; n < NB; n++) {
+    v16f ot;
+#pragma unroll
+    for (int pk = 0; pk < PK; pk++) {
+      const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
+      ot = (pk == 0) ? mfma_32x32x64_mx(pv_operand_mx<DV>(vt, 0, n, lane), pop[0], (v16f){}, sa, psc[0])
+                     : mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop[pk], ot, sa, psc[pk]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// 4 waves x 32 query rows of one query head; K/V tiles by direct global->LDS copies (two
+// stages), their scale blocks by ordinary loads stored to LDS before the end-of-tile barrier.
+template <int D, int DV>
+__global__ void __launch_bounds__(256, 2) fa8_prefill_mx_kernel(const KParams p) {
+  constexpr int BN = 128, NW = 4, BM = NW * 32;
+  constexpr int KTILE = BN * D, VTILE = BN * DV;
+  constexpr int KSC = BN * (D / 32), VSC = (BN / 32) * DV;     // scale bytes per tile
+  constexpr int STAGE = KTILE + VTILE + KSC + VSC;
+  constexpr int KINST = KTILE / 1024 / NW, VINST = VTILE / 1024 / NW;
+  static_assert(KTILE % (1024 * NW) == 0 && VTILE % (1024 * NW) == 0, "tile must split into 1 KB loads");
+  static_assert(D == 64 || D == 128, "MX prefill head dims");
+  constexpr int KCH = D / 16, VCH = DV / 16, NB = DV / 32, NBD = D / 32;
+  constexpr int VLANES = VSC / 16;                            // lanes loading the V scales
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hgrp = lane >> 5, lrow = lane & 31;
+
+  const int nwork = (int)gridDim.x;
+  const int L = (int)blockIdx.x;
+  const int xcd = L & 7, slot = L >> 3;
+  const int per = nwork >> 3, rem = nwork & 7;
+  const int w = xcd * per + min(xcd, rem) + slot;
+  const int g = p.g;
+  const int hg = w % g;
+  const int t1 = w / g;
+  const int mbi = t1 % p.nmb;
+  const int bk = t1 / p.nmb;
+  const int kvh = bk % p.hkv, b = bk / p.hkv;
+  const int mblock = p.causal ? p.nmb - 1 - mbi : mbi;
+  const int qh = kvh * g + hg;
+
+  const SeqInfo si = seq_info(p, b);
+  const int rb0 = mblock * BM;
+  if (rb0 >= si.sq) return;
+  const int rb1 = min(rb0 + BM, si.sq) - 1;
+  const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+  int wg_lo = rr.lo(rb0), wg_hi = rr.hi(rb1);
+  const int full_lo = rr.lo(rb1), full_hi = rr.hi(rb0);
+  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
+  const int t_begin = wg_lo / BN;
+  const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
+
+  const int qi = rb0 + wave * 32 + lrow;
+  const bool valid = qi <= rb1;
+  int my_lo = 0, my_hi = 0;
+  if (valid) {
+    my_lo = rr.lo(qi);
+    my_hi = rr.hi(qi);
+  }
+  const float c = p.scale_log2;
+
+  v8i qop[D / 64];
+  load_q_mx<D>(p.q + (int64_t)b * p.q_bs + (int64_t)qi * p.q_rs + (int64_t)qh * p.q_hs, valid, hgrp, qop);
+  int qsc[D / 64];
+  {
+    uint32_t qw = 0x7f7f7f7fu;
+    if (valid) {
+      const uint8_t* qs = p.q_mx + (int64_t)b * p.qmx_bs + (int64_t)qi * p.qmx_rs + (int64_t)qh * p.qmx_hs;
+      qw = (NBD == 4) ? *(const uint32_t*)qs : (uint32_t)*(const uint16_t*)qs;
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ks++) qsc[ks] = (int)((qw >> (8 * (2 * ks + hgrp))) & 0xffu);
+  }
+
+  const KvAddr ka = kv_addr(p, b, kvh);
+  uint32_t k_off[KINST], v_off[VINST];
+#pragma unroll
+  for (int i = 0; i < KINST; i++) {
+    const int pos = (wave * KINST + i) * 1024 + lane * 16;
+    const int row = pos / D, pc = (pos - row * D) >> 4;
+    k_off[i] = (uint32_t)(row * (int)ka.k_rs + swz<KCH>(pc, k_sv<D>(row)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < VINST; i++) {
+    const int pos = (wave * VINST + i) * 1024 + lane * 16;
+    const int row = pos / DV, pc = (pos - row * DV) >> 4;
+    v_off[i] = (uint32_t)(row * (int)ka.v_rs + swz<VCH>(pc, v_sv(row)) * 16);
+  }
+  auto dma_tile = [&](int t, int st) __attribute__((always_inline)) {
+    FA8_LDS uint8_t* kt = (FA8_LDS uint8_t*)smem + st * STAGE;
+    FA8_LDS uint8_t* vt = kt + KTILE;
+    const int j0 = t * BN;
+    const int rows = min(si.sk - j0, BN);
+    const v4i kr = buffer_rsrc(p.k + ka.kbase + (int64_t)j0 * ka.k_rs, (uint32_t)((rows - 1) * (int)ka.k_rs + D));
+    const v4i vr = buffer_rsrc(p.v + ka.vbase + (int64_t)j0 * ka.v_rs, (uint32_t)((rows - 1) * (int)ka.v_rs + DV));
+#pragma unroll
+    for (int i = 0; i < KINST; i++)
+      buffer_copy16_to_lds(kr, k_off[i], (uint32_t)reinterpret_cast<uintptr_t>(kt + (wave * KINST + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < VINST; i++)
+      buffer_copy16_to_lds(vr, v_off[i], (uint32_t)reinterpret_cast<uintptr_t>(vt + (wave * VINST + i) * 1024));
+  };
+  // Scale blocks of tile t: threads 0..BN-1 read the D/32 K scale bytes of key j0 + tid (keys
+  // past the sequence: any value, their scores are masked); threads BN..BN+VLANES-1 read 16
+  // bytes of the tile's BN/32 V scale rows (blocks past the sequence: any value, their P is 0).
+  const int64_t kmx_base = (int64_t)b * p.kmx_bs + (int64_t)kvh * p.kmx_hs;
+  const int64_t vmx_base = (int64_t)b * p.vmx_bs + (int64_t)kvh * p.vmx_hs;
+  const int nvblk = (si.sk + 31) / 32;
+  auto load_scales = [&](int t) __attribute__((always_inline)) -> v4i {
+    v4i x = {0x7f7f7f7f, 0x7f7f7f7f, 0x7f7f7f7f, 0x7f7f7f7f};
+    if (tid < BN) {
+      const int j = t * BN + tid;
+      if (j < si.sk) {
+        const uint8_t* src = p.k_mx + kmx_base + (int64_t)j * p.kmx_rs;
+        x[0] = (NBD == 4) ? *(const int*)src : (int)*(const uint16_t*)src;
+      }
+    } else if (tid < BN + VLANES) {
+      const int u = tid - BN;
+      const int blk = t * (BN / 32) + u / (DV / 16), col = (u % (DV / 16)) * 16;
+      if (blk < nvblk) x = ld_global16(p.v_mx + vmx_base + (int64_t)blk * p.vmx_ts + col);
+    }
+    return x;
+  };
+  auto store_scales = [&](v4i x, int st) __attribute__((always_inline)) {
+    FA8_LDS uint8_t* ks = (FA8_LDS uint8_t*)smem + st * STAGE + KTILE + VTILE;
+    if (tid < BN) {
+      if constexpr (NBD == 4) *(FA8_LDS int*)(ks + tid * 4) = x[0];
+      else *(FA8_LDS uint16_t*)(ks + tid * 2) = (uint16_t)x[0];
+    } else if (tid < BN + VLANES) {
+      *(FA8_LDS v4i*)(ks + KSC + (tid - BN) * 16) = x;
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.0f;
+  v16f oacc[NB];
+#pragma unroll
+  for (int n = 0; n < NB; n++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) oacc[n][r] = 0.0f;
+
+  // The scales of tile t+1 are read from global memory one iteration early and stored to LDS
+  // at the start of tile t, next to that tile's K/V copies: nothing conditional follows the
+  // tile's arithmetic in the loop body (the compiler would sink that arithmetic past it).
+  v4i sc_next = {0, 0, 0, 0};
+  if (t_begin < t_end) {
+    dma_tile(t_begin, 0);
+    store_scales(load_scales(t_begin), 0);
+    sc_next = load_scales(t_begin + 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  for (int t = t_begin; t < t_end; t++) {
+    const int st = (t - t_begin) & 1;
+    if (t + 1 < t_end) {
+      dma_tile(t + 1, st ^ 1);
+      store_scales(sc_next, st ^ 1);   // stage st^1 is not read during tile t
+      sc_next = load_scales(t + 2);    // lands before the end-of-tile wait
+    }
+    const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem + st * STAGE;
+    const int j0 = t * BN;
+    const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
+    attn_tile_mx<D, DV, BN>(kt, kt + KTILE, kt + KTILE + VTILE, kt + KTILE + VTILE + KSC, qop, qsc, c, need_mask,
+                            j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  if (!valid) return;
+  store_row<DV, false>(p, oacc, m_run, l_run, 1.0f, hgrp, b, 0, qi, qh, 0, 0.0f);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1628,6 +1984,16 @@ static hipError_t launch_decode_t(const KParams& kp, hipStream_t stream) {
 
 hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream) {
   FA8_DISPATCH(launch_prefill_t, d, dv, kp, stream);
+}
+hipError_t launch_prefill_mx(const KParams& kp, int d, int dv, hipStream_t stream) {
+  const int64_t nwork = (int64_t)kp.nmb * kp.hq * kp.batch;
+  if (d == 64 && dv == 64)
+    hipLaunchKernelGGL((fa8_prefill_mx_kernel<64, 64>), dim3((unsigned)nwork), dim3(256), 0, stream, kp);
+  else if (d == 128 && dv == 128)
+    hipLaunchKernelGGL((fa8_prefill_mx_kernel<128, 128>), dim3((unsigned)nwork), dim3(256), 0, stream, kp);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 // ---- several kv heads per wave: applicability and launch ----
 // Returns the kv heads per wave of fa8_decode_heads_kernel for this problem, or 0 when the

@@ -207,6 +207,44 @@ def with_mx(inp: AttnInputs, seed: int, lo: int = 122, hi: int = 132) -> AttnInp
                                v_descale=None, name=inp.name + "_mx")
 
 
+def _mx_blocks(x: torch.Tensor, axis: int):
+    """MXFP8 encoding of float32 x in blocks of 32 consecutive elements along `axis` (the tail
+    block zero-padded): E8M0 scale 2^X with X = ceil(log2(amax / 448)), the smallest power of two
+    that keeps the block's largest magnitude at or below 448 (clamped to [-127, 127]; X = -127
+    for an all-zero block), and E4M3 elements x / 2^X cast with round to nearest even (torch's
+    cast). Returns (uint8 codes shaped like x, uint8 scale bytes with that axis divided by 32)."""
+    x = x.movedim(axis, -1)
+    n = x.shape[-1]
+    nb = (n + 31) // 32
+    pad = torch.zeros(x.shape[:-1] + (nb * 32,), dtype=torch.float32)
+    pad[..., :n] = x
+    blk = pad.reshape(x.shape[:-1] + (nb, 32))
+    amax = blk.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax / 448.0)), torch.full_like(amax, -127.0))
+    e = e.clamp(-127, 127)
+    codes = (blk / torch.exp2(e)[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = codes.reshape(pad.shape)[..., :n].movedim(-1, axis).contiguous()
+    scales = (e + 127).to(torch.uint8).movedim(-1, axis).contiguous()
+    return codes.numpy(), scales.numpy()
+
+
+def make_mx(seed: int, batch: int, sq: int, sk: int, heads_q: int, heads_kv: int, d: int, dv: int,
+            causal: bool = False, window_left: int = -1, window_right: int = -1, v_mean: float = 0.0,
+            softmax_scale: float = 0.0, out_dtype: str = "bf16", name: str = "") -> AttnInputs:
+    """Fixed-length BSHD Q/K/V drawn N(0,1) in float32 (V shifted by v_mean) and encoded as MXFP8:
+    blocks of 32 along d for Q and K, along the keys for V (_mx_blocks)."""
+    g = torch.Generator().manual_seed(seed)
+    qf = torch.randn((batch, sq, heads_q, d), generator=g, dtype=torch.float32)
+    kf = torch.randn((batch, sk, heads_kv, d), generator=g, dtype=torch.float32)
+    vf = torch.randn((batch, sk, heads_kv, dv), generator=g, dtype=torch.float32) + v_mean
+    q, qs = _mx_blocks(qf, -1)
+    k, ks = _mx_blocks(kf, -1)
+    v, vs = _mx_blocks(vf, 1)
+    return AttnInputs(batch, heads_q, heads_kv, d, dv, q, k, v, sq, sk, softmax_scale=softmax_scale,
+                      causal=causal, window_left=window_left, window_right=window_right, out_dtype=out_dtype,
+                      name=name, q_mx=qs, k_mx=ks, v_mx=vs)
+
+
 def random_lengths(gen: torch.Generator, n: int, lo: int, hi: int) -> np.ndarray:
     """n integers uniform in [lo, hi] (inclusive)."""
     return torch.randint(lo, hi + 1, (n,), generator=gen).numpy().astype(np.int64)

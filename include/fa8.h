@@ -212,6 +212,51 @@ typedef struct {
 int64_t fa8_quantize_q_workspace_bytes(const fa8_quant_params* p);
 fa8_status fa8_quantize_q(const fa8_quant_params* p, void* workspace, void* stream);
 
+/*
+ * MXFP8 forward pass (the MXFP8 forward of the FlashAttention-4 MXFP8 page, sections 1, 2.1
+ * and 2.1.3): Q, K and V are E4M3FN elements with E8M0 block scales, one scale per 32
+ * elements along each product's contraction dimension: along d for Q and K, along the keys
+ * for V. An E8M0 scale is one unsigned byte e with value 2^(e - 127); 0xFF is NaN (OCP
+ * Microscaling Formats specification). The real value of an element is its E4M3 value times
+ * its block's scale. Both products run on the block-scaled MFMA: S = Q K^T with the Q and K
+ * scales, then O = P V with P converted online to MXFP8: for each query row and each block of
+ * 32 keys, the block's largest score x (log2 units, s * softmax_scale * log2 e) against the
+ * row's running max m gives the shared exponent X = ceil(x - m - log2 448): the smallest power
+ * of two that brings the block's largest P = 2^(x - m) to at most 448, so no element is clipped
+ * (the page derives its scale from the block amax's exponent and mantissa bits; the amax
+ * itself comes from the softmax's block maxima), clamped to [-127, 127]. The block stores
+ * E4M3(2^(s' - m - X)) (s' the scaled score, round to nearest even) with scale 2^X. The online
+ * softmax keeps the
+ * lazy rescale of fa8_fwd_prefill (the running max moves only when a tile's max exceeds it by
+ * more than 0.75); there is no 2^8 offset (the block scales cover the range). The row sum is
+ * taken over the stored P times its scales, and each tile's PV is accumulated from zero and
+ * folded into fp32 O as in fa8_fwd_prefill.
+ *
+ * p: as for fa8_fwd_prefill with these limits: (d, dv) = (64, 64) or (128, 128); fixed-length
+ *   Q and K/V (cu_seqlens_q, cu_seqlens_k, seqused_k and block_table NULL); the descales of p
+ *   must be absent (ptr NULL: the block scales replace them). Masks, GQA, softmax_scale, lse,
+ *   sink and out_dtype as for fa8_fwd_prefill.
+ * s: the three scale tensors (uint8 E8M0, device, caller owned; strides in bytes, last
+ *   dimension contiguous):
+ *   q: [batch, max_seqlen_q, heads_q, d/32]  element (b, i, h, c) at
+ *      q + b*q_batch_stride + i*q_row_stride + h*q_head_stride + c
+ *   k: [batch, max_seqlen_k, heads_kv, d/32] (same addressing with k_*)
+ *   v: [batch, ceil(max_seqlen_k/32), heads_kv, dv]: the scale of keys 32t .. 32t+31 of
+ *      column c at v + b*v_batch_stride + t*v_block_stride + kvh*v_head_stride + c
+ *   q and k pointers and strides must be multiples of d/32; v's pointer and strides multiples
+ *   of 16. Otherwise FA8_ERR_INVALID; other shapes or layouts FA8_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  const uint8_t* q;
+  int64_t q_batch_stride, q_row_stride, q_head_stride;
+  const uint8_t* k;
+  int64_t k_batch_stride, k_row_stride, k_head_stride;
+  const uint8_t* v;
+  int64_t v_batch_stride, v_block_stride, v_head_stride;
+} fa8_mx_scales;
+
+fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, void* stream);
+
 /* Runs the host-side validation of fa8_fwd_prefill (num_splits == 0) or of
  * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything. Needs no GPU. */
 fa8_status fa8_check_params(const fa8_fwd_params* p, int32_t num_splits);

@@ -194,6 +194,8 @@ def method_bound(inp, ref: np.ndarray) -> np.ndarray:
     _, sk = oracle.seqlens(inp)
     table = oracle.e4m3_table()
     vmax = float(np.nanmax(np.abs(table[inp.v])))
+    if getattr(inp, "v_mx", None) is not None:       # MXFP8 V: the largest block scale
+        vmax *= 2.0 ** (int(np.max(inp.v_mx)) - 127)
     dvmax = float(np.max(inp.v_descale)) if inp.v_descale is not None else 1.0
     out_rel = 2.0 ** -11 if inp.out_dtype == "fp16" else 2.0 ** -8
     e = 2.0 ** -4 / (1 - 2.0 ** -4)

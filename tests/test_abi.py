@@ -243,3 +243,43 @@ def test_kernels_use_no_scratch():
         if "fa8_prefill_kernel" in name or "fa8_decode_heads_kernel" in name:
             assert int(u["Occupancy"]) >= 2, (name, u)
     assert any("fa8_prefill_kernel" in n for n in usage) and any("fa8_decode_kernel" in n for n in usage)
+
+
+def test_prefill_mx_host_validation():
+    """fa8_fwd_prefill_mx rejects what it does not take before any launch (host pointers are
+    never dereferenced on these paths)."""
+    lib = binding.load()
+    q = torch.zeros((1, 64, 2, 128), dtype=torch.uint8)
+    k = torch.zeros((1, 64, 1, 128), dtype=torch.uint8)
+    v = torch.zeros((1, 64, 1, 128), dtype=torch.uint8)
+    qs = torch.zeros((1, 64, 2, 4), dtype=torch.uint8)
+    ks = torch.zeros((1, 64, 1, 4), dtype=torch.uint8)
+    vs = torch.zeros((1, 2, 1, 128), dtype=torch.uint8)
+    out = torch.zeros((1, 64, 2, 128), dtype=torch.bfloat16)
+
+    def call(qq=q, kk=k, vv=v, qsc=qs, ksc=ks, vsc=vs, **kw):
+        p = binding._params(qq, kk, vv, kw.get("cu_q"), None, None, None, kw.get("max_sq"), None,
+                            kw.get("dq"), None, None, 0.0, True, -1, -1)
+        binding._set_out(p, out if qq.shape[-1] == 128 else torch.zeros(tuple(qq.shape[:-1]) + (vv.shape[-1],),
+                                                                         dtype=torch.bfloat16), None, False)
+        m = binding.MXScales(qsc.data_ptr(), qsc.stride(0), qsc.stride(1), qsc.stride(2),
+                             ksc.data_ptr(), ksc.stride(0), ksc.stride(1), ksc.stride(2),
+                             vsc.data_ptr(), vsc.stride(0), vsc.stride(1), vsc.stride(2))
+        return lib.fa8_fwd_prefill_mx(ctypes.byref(p), ctypes.byref(m), None)
+
+    assert lib.fa8_fwd_prefill_mx(None, None, None) == binding.FA8_ERR_INVALID
+    # descales are replaced by the block scales
+    assert call(dq=torch.ones(())) == binding.FA8_ERR_INVALID
+    assert "descale" in binding.last_error()
+    # (96, 96) has no MX kernel
+    q96, k96, v96 = (torch.zeros(t.shape[:-1] + (96,), dtype=torch.uint8) for t in (q, k, v))
+    assert call(qq=q96, kk=k96, vv=v96, qsc=qs[..., :3].contiguous(), ksc=ks[..., :3].contiguous(),
+                vsc=vs[..., :96].contiguous()) == binding.FA8_ERR_UNSUPPORTED
+    # varlen Q is not taken
+    qv = torch.zeros((64, 2, 128), dtype=torch.uint8)
+    cu = torch.tensor([0, 64], dtype=torch.int32)
+    assert call(qq=qv, cu_q=cu, max_sq=64) == binding.FA8_ERR_UNSUPPORTED
+    # V scale rows must keep 16-byte alignment
+    vs_bad = torch.zeros((1, 2, 1, 136), dtype=torch.uint8)[..., :128]
+    assert call(vsc=vs_bad) == binding.FA8_ERR_INVALID
+    assert "16" in binding.last_error()

@@ -113,3 +113,47 @@ def test_nan_scale_code_propagates(oracle_lib):
     assert np.isnan(o[0, :, :g, 5]).all()             # every row of that kv head's q heads
     assert np.isfinite(np.delete(o[0, :, :g], 5, axis=-1)).all()
     assert np.isfinite(o[1]).all() and np.isfinite(o[0, :, g:]).all()
+
+
+# ----------------------------------------------------------------------------------------
+# The MXFP8 method emulator (diagnostic) and the MX input encoding
+# ----------------------------------------------------------------------------------------
+
+def test_mx_encoding_keeps_block_max_in_range():
+    # make_mx's blocks: largest magnitude of every block in [224, 448] after scaling and rounding, and
+    # codes times scales reproduce the float32 draws to E4M3 precision
+    from oracle import emulator_mx
+    inp = gen.make_mx(30, 1, 70, 90, 2, 1, 64, 64)
+    t = oracle.e4m3_table()
+    qb = np.abs(t[inp.q]).reshape(1, 70, 2, 2, 32).max(axis=-1)
+    assert (qb >= 224).all() and (qb <= 448).all()          # E4M3 rounding may land on 224
+    vb = np.abs(t[np.concatenate([inp.v, np.zeros((1, 6, 1, 64), np.uint8)], axis=1)]).reshape(1, 3, 32, 1, 64).max(axis=2)
+    assert (vb >= 224).all() and (vb <= 448).all()
+    q, k, v = emulator_mx.dequantize(inp)
+    assert 0.5 < np.std(q) < 1.5 and 0.5 < np.std(v) < 1.5
+
+
+def test_emulator_mx_ceil_rule_never_clips_floor_rule_clips(oracle_lib):
+    # the shared exponent ceil(log2(amax / 448)) keeps every P of a block at or below 448; OCP's
+    # floor(log2 amax) - 8 lets the block's largest P reach [256, 512) and clips some at 448
+    from oracle import emulator_mx
+    inp = gen.make_mx(31, 1, 64, 256, 2, 1, 64, 64, causal=True)
+    s1, s2 = {}, {}
+    emulator_mx.emulate_mx(inp, rule="ceil", stats=s1)
+    emulator_mx.emulate_mx(inp, rule="floor", stats=s2)
+    assert s1["clipped"] == 0 and s2["clipped"] > 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_emulator_mx_tracks_oracle(oracle_lib, causal):
+    # on N(0,1) data encoded as MXFP8, the method's own error stays inside the stated tolerance,
+    # and the clipping rule is worse than the ceil rule on the same input
+    from oracle import emulator_mx
+    inp = gen.make_mx(32, 2, 100, 300, 4, 2, 128, 128, causal=causal)
+    ro, rl = oracle.attention_full(inp)
+    eo, el = emulator_mx.emulate_mx(inp, rule="ceil")
+    fo, _ = emulator_mx.emulate_mx(inp, rule="floor")
+    assert np.all(np.abs(eo - ro) <= 2e-2 + 2e-2 * np.abs(ro))
+    fin = np.isfinite(rl)
+    assert np.max(np.abs(el[fin] - rl[fin])) <= -math.log(1 - 2.0 ** -4)
+    assert np.sqrt(np.mean((fo - ro) ** 2)) > np.sqrt(np.mean((eo - ro) ** 2))
