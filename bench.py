@@ -206,12 +206,32 @@ def bench_prefill(inp, steps: int, warmup: int, dev):
     return (t1 - t0) * 1e3 / steps, kernel_ms
 
 
+def bench_prefill_mx(inp, steps: int, warmup: int, dev):
+    """Per-launch kernel time (HIP events) of the MXFP8 prefill on an MX-encoded input."""
+    q, k, v = (to_dev(x, dev) for x in (inp.q, inp.k, inp.v))
+    qs, ks, vs = (to_dev(x, dev) for x in (inp.q_mx, inp.k_mx, inp.v_mx))
+    out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=torch.bfloat16, device=dev)
+    kw = dict(causal=inp.causal, window_left=inp.window_left, window_right=inp.window_right, out=out)
+    for _ in range(warmup):
+        binding.prefill_mx(q, k, v, qs, ks, vs, **kw)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        binding.prefill_mx(q, k, v, qs, ks, vs, **kw)
+        b.record()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all(), "non-finite MX prefill output"
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
 def other_workloads(args, dev) -> dict:
     """Figures of the remaining measured workloads, reported beside the headline (not part of
     `value`): long-KV decode (4 sequences of 131072 keys, 8/1 heads, 64-token pages; GB/s of the
-    decode step and of its kernel), the causal prefill workload with a learnable sink, and the
-    mixed-shape varlen prefill (8 sequences, window 1024, fp16 out; TFLOP/s of the visible pairs)
-    for (d, dv) = (256, 256) and (192, 128)."""
+    decode step and of its kernel), the causal prefill workload with a learnable sink, the Q
+    quantizer, the MXFP8 prefill on the causal prefill shape, and the mixed-shape varlen prefill
+    (8 sequences, window 1024, fp16 out; TFLOP/s of the visible pairs) for (d, dv) = (256, 256)
+    and (192, 128)."""
     out = {}
     lk = gen.long_kv_decode(3)
     ms, kms, S = bench_decode(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev)
@@ -248,6 +268,15 @@ def other_workloads(args, dev) -> dict:
                                         "kernel_pct_of_hbm_peak": round(100 * qbytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                                         "note": "two launches (block maxima, then codes): Q is read twice"}
     del qb, q8
+    # the MXFP8 variant on the causal prefill shape: N(0,1) data encoded as MXFP8 (E4M3 elements,
+    # E8M0 scales per 32 elements of d for Q/K and per 32 keys for V)
+    mx = gen.make_mx(2, 2, 8192, 8192, 32, 8, 128, 128, causal=True, name="mxfp8_causal_prefill_b2_s8192_h32x8_d128")
+    kms = bench_prefill_mx(mx, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
+    fl = prefill_flop(mx)
+    out["mxfp8_causal_prefill"] = {"workload": mx.name, "unit": "TFLOP/s",
+                                   "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
+                                   "kernel_pct_of_fp8_peak": round(100 * fl / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2)}
+    del mx
     for d, dv in ((256, 256), (192, 128)):
         mv = gen.mixed_varlen(4, d=d, dv=dv)
         ms, kms = bench_prefill(mv, max(5, args.prefill_steps // 2), max(5, args.prefill_warmup // 5), dev)
