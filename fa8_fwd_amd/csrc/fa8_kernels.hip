@@ -801,10 +801,10 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
 //    scales of key block 2pk+h.
 // Per query row and 32-key block, the block's max x_b (log2 units) gives the shared exponent
 // X = ceil(x_b - m - log2 448) (m the running max), the smallest power of two that brings the
-// block's largest P = 2^(x_b - m) to at most 448, clamped to [-127, 127]; P = 2^(x - m - X) is
-// rounded to E4M3 with scale byte X + 127 (a min with 448 guards against exp2 rounding). Each
-// block's max comes from the row max's own reduction (two lanes hold a block's 32 keys), so no
-// extra pass over P is needed.
+// block's largest P = 2^(x_b - m) to at most 448 (computed with a margin of a few ulps, so that
+// fp32 rounding cannot push it past 448), clamped to [-127, 127]; P = 2^(x - m - X) is rounded
+// to E4M3 with scale byte X + 127. Each block's max comes from the row max's own reduction (two
+// lanes hold a block's 32 keys), so no extra pass over P is needed.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ v16f mfma_32x32x64_mx(v8i a, v8i b, v16f c, int sa, int sb) {
   // E4M3 operands; opsel 0 takes each lane's scale from byte 0 of sa / sb
@@ -898,56 +898,70 @@ __device__ __forceinline__ void attn_tile_mx(const FA8_LDS uint8_t* kt, const FA
   // ---- P per 32-key block: shared exponent X, E4M3(2^(x - m - X)), scale X + 127 ----
   int pscale[KB];
   float nbk[KB];
+  // X is raised by a margin of a few fp32 ulps of m (and exp2's own), so that the largest P of a
+  // block cannot round past 448 and no clamp per element is needed
+  const float margin = __builtin_fmaf(fabsf(m_run), 0x1p-21f, 0x1p-12f);
 #pragma unroll
   for (int kb = 0; kb < KB; kb++) {
     const float y = bmax[kb] * c - m_run;                   // -inf for an all-masked block
-    const float xe = (m_run == kNegInf) ? -127.0f : fmaxf(ceilf(y - kLog2E4M3Max), -127.0f);
+    const float xe = (m_run == kNegInf) ? -127.0f : fmaxf(ceilf(y - kLog2E4M3Max + margin), -127.0f);
     pscale[kb] = (int)xe + 127;
     nbk[kb] = (m_run == kNegInf) ? 0.0f : -(m_run + xe);
   }
+  // P of each 64-key half, its row-sum MFMA and its PV MFMAs (V block scale x P block scale).
+  // At dv = 128 the PV MFMAs of a half follow its own exponentials, so they overlap those of the
+  // next half (as in attn_tile); otherwise each column block goes after all of P.
+  constexpr bool kOverlap = PK > 1 && NB == 4;
+  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  const FA8_LDS uint8_t* vsc_lane = vsc + hgrp * DV + lrow;        // block hgrp, column lrow
   v8i pop[PK];
   int psc[PK];
+  v16f rs, ot[kOverlap ? NB : 1];
 #pragma unroll
   for (int pk = 0; pk < PK; pk++) {
 #pragma unroll
     for (int w = 0; w < 8; w++) {
       const int kb = 2 * pk + (w >> 2), r0 = 4 * (w & 3);
-      const float p0 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 0], c, nbk[kb])), 448.0f);
-      const float p1 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 1], c, nbk[kb])), 448.0f);
-      const float p2 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 2], c, nbk[kb])), 448.0f);
-      const float p3 = fminf(fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nbk[kb])), 448.0f);
+      const float p0 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 0], c, nbk[kb]));
+      const float p1 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 1], c, nbk[kb]));
+      const float p2 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 2], c, nbk[kb]));
+      const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nbk[kb]));
       int word = cvt_pk_fp8_lo(p0, p1);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
       pop[pk][w] = word;
     }
     psc[pk] = hgrp ? pscale[2 * pk + 1] : pscale[2 * pk];   // this lane half's key block
-  }
-
-  // ---- row sum of the stored P times its scales, on the block-scaled MFMA ----
-  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
-  v16f rs = mfma_32x32x64_mx(ones, pop[0], (v16f){}, 127, psc[0]);
+    if constexpr (kOverlap) {
 #pragma unroll
-  for (int pk = 1; pk < PK; pk++) rs = mfma_32x32x64_mx(ones, pop[pk], rs, 127, psc[pk]);
+      for (int n = 0; n < NB; n++) {
+        __builtin_amdgcn_sched_barrier(0);   // one V operand read ahead at a time
+        const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
+        ot[n] = (pk == 0) ? mfma_32x32x64_mx(pv_operand_mx<DV>(vt, 0, n, lane), pop[0], (v16f){}, sa, psc[0])
+                          : mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop[pk], ot[n], sa, psc[pk]);
+      }
+    }
+    // row sum of the stored P times its scales
+    rs = (pk == 0) ? mfma_32x32x64_mx(ones, pop[0], (v16f){}, 127, psc[0])
+                   : mfma_32x32x64_mx(ones, pop[pk], rs, 127, psc[pk]);
+  }
   l_run = alpha * l_run + rs[0];
 
-  // ---- O_tile = V^T P^T from zero per column block (V block scale x P block scale), then
-  //      O = alpha O + O_tile ----
-  const FA8_LDS uint8_t* vsc_lane = vsc + hgrp * DV + lrow;        // block hgrp, column lrow
-  // (scheduling barriers: without them the compiler reads every V operand of the tile during
-  // the exponentials and runs out of registers)
-  __builtin_amdgcn_sched_barrier(0);
+  // ---- O = alpha O + O_tile ----
+  if constexpr (!kOverlap) __builtin_amdgcn_sched_barrier(0);   // keeps the V reads out of the exponentials
 #pragma unroll
   for (int n = 0; n < NB; n++) {
-    v16f ot;
+    if constexpr (!kOverlap) {
 #pragma unroll
-    for (int pk = 0; pk < PK; pk++) {
-      const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
-      ot = (pk == 0) ? mfma_32x32x64_mx(pv_operand_mx<DV>(vt, 0, n, lane), pop[0], (v16f){}, sa, psc[0])
-                     : mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop[pk], ot, sa, psc[pk]);
+      for (int pk = 0; pk < PK; pk++) {
+        const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
+        ot[0] = (pk == 0) ? mfma_32x32x64_mx(pv_operand_mx<DV>(vt, 0, n, lane), pop[0], (v16f){}, sa, psc[0])
+                          : mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop[pk], ot[0], sa, psc[pk]);
+      }
     }
+    const v16f& t = ot[kOverlap ? n : 0];
 #pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], ot[r]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], t[r]);
+    if constexpr (!kOverlap) __builtin_amdgcn_sched_barrier(0);
   }
 }
 

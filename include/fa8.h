@@ -223,6 +223,7 @@ fa8_status fa8_quantize_q(const fa8_quant_params* p, void* workspace, void* stre
  * 32 keys, the block's largest score x (log2 units, s * softmax_scale * log2 e) against the
  * row's running max m gives the shared exponent X = ceil(x - m - log2 448): the smallest power
  * of two that brings the block's largest P = 2^(x - m) to at most 448, so no element is clipped
+ * (evaluated with a margin of a few fp32 ulps of m, which can raise X by one next to an integer)
  * (the page derives its scale from the block amax's exponent and mantissa bits; the amax
  * itself comes from the softmax's block maxima), clamped to [-127, 127]. The block stores
  * E4M3(2^(s' - m - X)) (s' the scaled score, round to nearest even) with scale 2^X. The online
