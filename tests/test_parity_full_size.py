@@ -13,6 +13,7 @@ import oracle
 from fa8_fwd_amd import inputs as gen
 
 from helpers import ATOL, LSE_ATOL, LSE_METHOD, RTOL, run_decode, run_prefill
+from test_mx_gpu import run_mx
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +68,8 @@ def _method_bound_rows(inp, rows, ref):
     a, _ = oracle.attention(absinp, rows=rows)
     _, sk = oracle.seqlens(inp)
     vmax = float(np.nanmax(np.abs(oracle.e4m3_table()[inp.v])))
+    if getattr(inp, "v_mx", None) is not None:       # MXFP8 V: the largest block scale
+        vmax *= 2.0 ** (int(np.max(inp.v_mx)) - 127)
     dvmax = float(np.max(inp.v_descale)) if inp.v_descale is not None else 1.0
     out_rel = 2.0 ** -11 if inp.out_dtype == "fp16" else 2.0 ** -8
     e = 2.0 ** -4 / (1 - 2.0 ** -4)
@@ -140,3 +143,12 @@ def test_mixed_varlen_full_size_sampled_rows(d, dv):
     got, glse = run_prefill(inp)
     assert np.all(np.isfinite(got))
     _check_rows(inp, got, glse, _sample_rows(inp, 24, seed=11), f"mixed varlen d{d} dv{dv} (sampled rows)")
+
+
+def test_mxfp8_causal_prefill_full_size_sampled_rows():
+    # the MXFP8 workload the benchmark times: B=2, 8192 x 8192, 32/8 heads, d=128, N(0,1) data
+    # encoded as MXFP8 (E8M0 scales per 32 elements of d for Q/K, per 32 keys for V)
+    inp = gen.make_mx(2, 2, 8192, 8192, 32, 8, 128, 128, causal=True)
+    got, glse = run_mx(inp)
+    assert np.all(np.isfinite(got))
+    _check_rows(inp, got, glse, _sample_rows(inp, 32, seed=9), "mxfp8 causal prefill b2 s8192 (sampled rows)")
