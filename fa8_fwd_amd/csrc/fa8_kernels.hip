@@ -1811,39 +1811,41 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   const int q0 = c.cu_q ? c.cu_q[b] : 0;
   const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
   if (i >= sq) return;
-  // splits in batches of 8 whose loads are all issued before any is used (the loop is bound by
-  // memory latency, not bandwidth)
+  // One pass over the splits in batches of 8 whose LSE and partial loads are all issued before
+  // any is used (the kernel is bound by memory latency, not bandwidth): a running max, with the
+  // sums rescaled when a batch raises it, so a problem of up to 8 splits costs one round trip.
   constexpr int SB = 8;
   // a sink logit is one more denominator term without a value
   const float z = c.sink ? c.sink[h] : kNegInf;
   float mx = z;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = (z == kNegInf) ? 0.0f : 1.0f;          // e^(z - mx) with mx = z
   for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
     float ls[SB];
+    v4f o[SB];
 #pragma unroll
-    for (int k = 0; k < SB; k++) ls[k] = (s0 + k < c.nsplit) ? c.lse_part[(int64_t)(s0 + k) * rows + row] : kNegInf;
+    for (int k = 0; k < SB; k++) {
+      const bool in = s0 + k < c.nsplit;
+      ls[k] = in ? c.lse_part[(int64_t)(s0 + k) * rows + row] : kNegInf;
+      o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)(s0 + k) * rows + row) * c.dv + 4 * q)
+                : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float bm = mx;
 #pragma unroll
-    for (int k = 0; k < SB; k++) mx = fmaxf(mx, ls[k]);
-  }
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float den = (z == kNegInf) ? 0.0f : __expf(z - mx);
-  if (mx != kNegInf) {
-    for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
-      float ls[SB];
-      v4f o[SB];
+    for (int k = 0; k < SB; k++) bm = fmaxf(bm, ls[k]);
+    if (bm == kNegInf) continue;                     // every split so far empty
+    if (bm != mx) {                                  // rescale what the earlier batches added
+      const float r = (mx == kNegInf) ? 0.0f : __expf(mx - bm);
+      den *= r;
+      acc *= r;
+      mx = bm;
+    }
 #pragma unroll
-      for (int k = 0; k < SB; k++) {
-        const bool in = s0 + k < c.nsplit;
-        ls[k] = in ? c.lse_part[(int64_t)(s0 + k) * rows + row] : kNegInf;
-        o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)(s0 + k) * rows + row) * c.dv + 4 * q)
-                  : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-      }
-#pragma unroll
-      for (int k = 0; k < SB; k++) {
-        // an empty split (LSE = -inf) has weight 0 and O = 0
-        const float w = (ls[k] == kNegInf) ? 0.0f : __expf(ls[k] - mx);
-        den += w;
-        acc += w * o[k];
-      }
+    for (int k = 0; k < SB; k++) {
+      // an empty split (LSE = -inf) has weight 0 and O = 0
+      const float w = (ls[k] == kNegInf) ? 0.0f : __expf(ls[k] - mx);
+      den += w;
+      acc += w * o[k];
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
