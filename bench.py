@@ -146,7 +146,7 @@ def device_args(inp, dev):
 EVENT_EVERY = 10
 
 
-def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None):
+def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None, event_every: int = EVENT_EVERY):
     q, k, v, kw = device_args(inp, dev)
     B, HQ, SQ, DV = inp.batch, inp.heads_q, inp.max_seqlen_q, inp.dv
     S = num_splits or binding.decode_num_splits_for(q, k, v, **kw)
@@ -164,10 +164,10 @@ def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None):
 
     for _ in range(warmup):
         step()
-    # HIP events around the decode kernel of every EVENT_EVERY-th timed step (an event pair on
-    # every step adds about 6 us to a 120 us step; one in ten adds under 1 us)
-    # (not the first timed step, which starts on an idle GPU)
-    sampled = list(range(min(EVENT_EVERY // 2, steps - 1), steps, EVENT_EVERY))
+    # HIP events around the decode kernel of every event_every-th timed step (an event pair on
+    # every step adds about 6 us to a 120 us step; one in ten adds under 1 us), not the first
+    # timed step, which starts on an idle GPU
+    sampled = list(range(min(event_every // 2, steps - 1), steps, event_every))
     evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -242,7 +242,9 @@ def other_workloads(args, dev) -> dict:
     and (192, 128)."""
     out = {}
     lk = gen.long_kv_decode(3)
-    ms, kms, S = bench_decode(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev)
+    # (events on every step: this kernel is short, so a few samples would mostly show dispatch
+    # jitter; the step figure then carries the event overhead)
+    ms, kms, S = bench_decode(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev, event_every=1)
     kb = decode_kernel_bytes(lk)
     out["long_kv_decode"] = {"workload": lk.name, "num_splits": S, "unit": "GB/s",
                              "step_value": round(decode_step_bytes(lk) / (ms * 1e-3) / 1e9, 2),
