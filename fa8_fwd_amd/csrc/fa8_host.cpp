@@ -294,6 +294,10 @@ fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream) {
   if (validate_env() && (st = validate_device_data(p)) != FA8_OK) return st;
   fa8::KParams k = make_kparams(p);
   k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
+  // lengths read on the device: deal the (batch, kv head) groups to the XCDs round-robin
+  if (p->cu_seqlens_q || p->cu_seqlens_k || p->seqused_k)
+    k.bk8 = (int32_t)(((int64_t)p->batch * p->heads_kv + 7) / 8);
+  if (fa8::prefill_grid(k) >= ((int64_t)1 << 31)) return fail(FA8_ERR_INVALID, "prefill grid too large");
   hipError_t e = fa8::launch_prefill(k, p->d, p->dv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA8_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -326,6 +330,7 @@ fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, v
   if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
   fa8::KParams k = make_kparams(p);
   k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
+  if (fa8::prefill_grid(k) >= ((int64_t)1 << 31)) return fail(FA8_ERR_INVALID, "prefill grid too large");
   k.q_mx = s->q; k.qmx_bs = s->q_batch_stride; k.qmx_rs = s->q_row_stride; k.qmx_hs = s->q_head_stride;
   k.k_mx = s->k; k.kmx_bs = s->k_batch_stride; k.kmx_rs = s->k_row_stride; k.kmx_hs = s->k_head_stride;
   k.v_mx = s->v; k.vmx_bs = s->v_batch_stride; k.vmx_ts = s->v_block_stride; k.vmx_hs = s->v_head_stride;

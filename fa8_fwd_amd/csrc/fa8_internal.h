@@ -30,6 +30,7 @@ struct KParams {
   float* lse; int64_t l_bs, l_hs, l_rs;
   float* o_part; float* lse_part; int32_t nsplit;
   int32_t nmb;                // row blocks per (batch, head) (decode) or per (batch, q head) (prefill)
+  int32_t bk8;                // prefill with per-sequence lengths: ceil(batch * hkv / 8), else 0
   const float* sink;          // [hq] sink logits or null (prefill finalize only)
   // MXFP8 block scales (E8M0 bytes; strides in bytes), MX prefill only
   const uint8_t* q_mx; int64_t qmx_bs, qmx_rs, qmx_hs;
@@ -61,6 +62,13 @@ hipError_t launch_quantize_q(const QParams& qp, hipStream_t stream);
 
 // Rows per workgroup of the prefill kernel and of the decode kernel.
 constexpr int kPrefillRows = 128;
+
+// Workgroups of a prefill launch: one per (row block, q head, batch), or, with per-sequence
+// lengths, 8 * bk8 * nmb * g (the round-robin deal of (batch, kv head) groups over the 8 XCDs
+// rounds the group count up to a multiple of 8).
+inline int64_t prefill_grid(const KParams& k) {
+  return k.bk8 > 0 ? (int64_t)8 * k.bk8 * k.nmb * k.g : (int64_t)k.nmb * k.hq * k.batch;
+}
 constexpr int kDecodeRows = 32;
 constexpr int kKvTile = 64;
 

@@ -639,7 +639,40 @@ __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[D
 // LDS by direct global->LDS loads (two stages, so the next tile lands while this one is used).
 // Workgroups are numbered so that each XCD (workgroup id mod 8) receives a contiguous run of
 // the work list, ordered by (batch, kv head), so the workgroups that share K/V share an L2.
+// With per-sequence lengths (varlen or seqused_k) a contiguous run would hand whole sequences
+// of very different lengths to single XCDs, so there (p.bk8 > 0) the (batch, kv head) groups
+// are dealt to the XCDs round-robin instead, row block by row block, the deal rotating by
+// one XCD every kRankChunk row blocks: every XCD sees every sequence, and the row blocks of
+// one group that lie close together (and share K/V) still meet in one L2.
 // ------------------------------------------------------------------------------------------
+constexpr int kRankChunk = 8;
+
+struct PrefillWork {
+  int bk, mbi, hg;   // (batch * hkv + kv head), row-block rank, q head within the kv group
+};
+
+__device__ __forceinline__ PrefillWork prefill_work(const KParams& p) {
+  const int L = (int)blockIdx.x;
+  const int xcd = L & 7, slot = L >> 3;
+  const int g = p.g;
+  PrefillWork wk;
+  if (p.bk8 == 0) {
+    const int nwork = (int)gridDim.x;
+    const int per = nwork >> 3, rem = nwork & 7;
+    const int w = xcd * per + min(xcd, rem) + slot;
+    wk.hg = w % g;
+    const int t1 = w / g;
+    wk.mbi = t1 % p.nmb;
+    wk.bk = t1 / p.nmb;
+  } else {
+    // grid = 8 * bk8 * nmb * g; XCD x takes at rank r the groups bk = ((x - r/kRankChunk) mod 8) + 8 i
+    wk.hg = slot % g;
+    const int t1 = slot / g;
+    wk.mbi = t1 / p.bk8;
+    wk.bk = ((xcd - wk.mbi / kRankChunk) & 7) + 8 * (t1 % p.bk8);   // >= batch * hkv: no work
+  }
+  return wk;
+}
 template <int D, int DV, int BN, bool PAGED>
 __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   constexpr int NW = 4, BM = NW * 32;
@@ -656,17 +689,11 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   const int hgrp = lane >> 5, lrow = lane & 31;
 
   // ---- XCD-aware work index ----
-  const int nwork = (int)gridDim.x;
-  const int L = (int)blockIdx.x;
-  const int xcd = L & 7, slot = L >> 3;
-  const int per = nwork >> 3, rem = nwork & 7;
-  const int w = xcd * per + min(xcd, rem) + slot;
   const int g = p.g;
-  const int hg = w % g;
-  const int t1 = w / g;
-  const int mbi = t1 % p.nmb;
-  const int bk = t1 / p.nmb;            // b * hkv + kvh
-  const int kvh = bk % p.hkv, b = bk / p.hkv;
+  const PrefillWork wk = prefill_work(p);
+  if (wk.bk >= p.batch * p.hkv) return;   // uniform: a slot of the round-robin deal with no group
+  const int hg = wk.hg, mbi = wk.mbi;
+  const int kvh = wk.bk % p.hkv, b = wk.bk / p.hkv;
   const int mblock = p.causal ? p.nmb - 1 - mbi : mbi;   // causal: heaviest row blocks first
   const int qh = kvh * g + hg;
 
@@ -1950,7 +1977,7 @@ constexpr int prefill_tile() { return (D + DV) <= 256 ? 128 : 64; }
 
 template <int D, int DV>
 static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
-  const int64_t nwork = (int64_t)kp.nmb * kp.hq * kp.batch;
+  const int64_t nwork = prefill_grid(kp);
   if (kp.page_shift >= 0)
     hipLaunchKernelGGL((fa8_prefill_kernel<D, DV, prefill_tile<D, DV>(), true>), dim3((unsigned)nwork), dim3(256), 0,
                        stream, kp);
@@ -2002,7 +2029,7 @@ hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream) 
   FA8_DISPATCH(launch_prefill_t, d, dv, kp, stream);
 }
 hipError_t launch_prefill_mx(const KParams& kp, int d, int dv, hipStream_t stream) {
-  const int64_t nwork = (int64_t)kp.nmb * kp.hq * kp.batch;
+  const int64_t nwork = prefill_grid(kp);   // fixed-length inputs only: bk8 = 0
   if (d == 64 && dv == 64)
     hipLaunchKernelGGL((fa8_prefill_mx_kernel<64, 64>), dim3((unsigned)nwork), dim3(256), 0, stream, kp);
   else if (d == 128 && dv == 128)
