@@ -1908,56 +1908,61 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
   const int q0 = c.cu_q ? c.cu_q[b] : 0;
   const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
   if (i >= sq) return;   // uniform over the workgroup
-  float mx = kNegInf;
+  // one pass per split lane: a running maximum rescales the lane's weight sum and accumulator
+  // whenever a batch of LSEs raises it, so every partial is read once
+  float mx = kNegInf, den = 0.0f;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bool has_cols = q < tpr;
   for (int s0 = sp; s0 < c.nsplit; s0 += SB * SP) {
     float ls[SB];
+    v4f o[SB];
 #pragma unroll
     for (int k = 0; k < SB; k++) {
       const int sidx = s0 + k * SP;
-      ls[k] = sidx < c.nsplit ? c.lse_part[(int64_t)sidx * rows + row] : kNegInf;
+      const bool in = sidx < c.nsplit;
+      ls[k] = in ? c.lse_part[(int64_t)sidx * rows + row] : kNegInf;
+      o[k] = (in && has_cols)
+                 ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)sidx * rows + row) * c.dv + 4 * q)
+                 : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float bm = mx;
+#pragma unroll
+    for (int k = 0; k < SB; k++) bm = fmaxf(bm, ls[k]);
+    if (bm == kNegInf) continue;    // every split so far empty
+    if (bm != mx) {
+      const float r = (mx == kNegInf) ? 0.0f : __expf(mx - bm);
+      den *= r;
+      acc *= r;
+      mx = bm;
     }
 #pragma unroll
-    for (int k = 0; k < SB; k++) mx = fmaxf(mx, ls[k]);
-  }
-  if (q == 0) s_mx[sp] = mx;
-  __syncthreads();
-  // a sink logit is one more denominator term without a value (added once, below)
-  const float z = c.sink ? c.sink[h] : kNegInf;
-  mx = fmaxf(mx, z);
-#pragma unroll 1
-  for (int k = 0; k < SP; k++) mx = fmaxf(mx, s_mx[k]);
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float den = 0.0f;
-  if (mx != kNegInf && q < tpr) {
-    for (int s0 = sp; s0 < c.nsplit; s0 += SB * SP) {
-      float ls[SB];
-      v4f o[SB];
-#pragma unroll
-      for (int k = 0; k < SB; k++) {
-        const int sidx = s0 + k * SP;
-        const bool in = sidx < c.nsplit;
-        ls[k] = in ? c.lse_part[(int64_t)sidx * rows + row] : kNegInf;
-        o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)sidx * rows + row) * c.dv + 4 * q)
-                  : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-      }
-#pragma unroll
-      for (int k = 0; k < SB; k++) {
-        const float w = (ls[k] == kNegInf) ? 0.0f : __expf(ls[k] - mx);   // empty split: weight 0
-        den += w;
-        acc += w * o[k];
-      }
+    for (int k = 0; k < SB; k++) {
+      const float w = (ls[k] == kNegInf) ? 0.0f : __expf(ls[k] - mx);   // empty split: weight 0
+      den += w;
+      acc += w * o[k];
     }
   }
   s_acc[sp][q] = acc;
-  if (q == 0) s_den[sp] = den;
+  if (q == 0) {
+    s_mx[sp] = mx;
+    s_den[sp] = den;
+  }
   __syncthreads();
   if (sp != 0 || q >= tpr) return;
+  // a sink logit is one more denominator term without a value (added once, here)
+  const float z = c.sink ? c.sink[h] : kNegInf;
+  mx = z;
+#pragma unroll 8
+  for (int k = 0; k < SP; k++) mx = fmaxf(mx, s_mx[k]);
   den = (z == kNegInf) ? 0.0f : __expf(z - mx);
   acc = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 1
-  for (int k = 0; k < SP; k++) {
-    den += s_den[k];
-    acc += s_acc[k][q];
+  if (mx != kNegInf) {
+#pragma unroll 8
+    for (int k = 0; k < SP; k++) {
+      const float r = (s_mx[k] == kNegInf) ? 0.0f : __expf(s_mx[k] - mx);   // lane with no split: 0
+      den += r * s_den[k];
+      acc += r * s_acc[k][q];
+    }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   const int64_t ooff = (c.cu_q ? (int64_t)(q0 + i) * c.o_rs : (int64_t)b * c.o_bs + (int64_t)i * c.o_rs) +
