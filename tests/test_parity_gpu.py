@@ -62,6 +62,14 @@ def test_prefill_sq_longer_than_sk_has_empty_rows():
     assert np.all(got[0, :80] == 0) and np.all(np.isneginf(glse[0, :, :80]))
 
 
+@pytest.mark.parametrize("wl,wr", [(100, 30), (-1, 50), (0, 0)])
+def test_prefill_two_sided_window(wl, wr):
+    # non-causal local windows: row i sees keys i' - wl .. i' + wr, i' = i + Sk - Sq (bottom-right
+    # alignment); (0, 0) leaves each row its own key alone
+    inp = gen.make_dense(30 + max(wl, 0) + wr, 2, 203, 331, 4, 2, 128, 128, window_left=wl, window_right=wr)
+    _prefill_check(inp, f"prefill window ({wl}, {wr}) q203 k331", strict=False)
+
+
 def test_prefill_varlen_window_fp16():
     inp = gen.mixed_varlen(4, d=256, dv=256, nseq=4, lo=64, hi=700, window=128)
     # 128-key windows and causal starts of sequences: few keys per row, the method's bound applies
@@ -176,6 +184,14 @@ def test_decode_multi_token(sq, page, causal, wl):
     inp = gen.make_paged(10 + sq, sk, 8, 2, 128, 128, page_size=page, sq=sq, varlen_q=True, causal=causal,
                          window_left=wl, descales=(("uniform", 0.5, 2.0),) * 3)
     _decode_check(inp, 4, f"decode sq{sq} page{page} causal{causal} wl{wl}", strict=False)
+
+
+@pytest.mark.parametrize("page", [16, 64])
+def test_decode_two_sided_window(page):
+    # four query tokens per sequence, non-causal window reaching 100 keys back and 2 ahead
+    inp = gen.make_paged(40 + page, [300, 1000, 64, 1], 8, 2, 128, 128, page_size=page, sq=4, varlen_q=True,
+                         window_left=100, window_right=2, descales=(("uniform", 0.5, 2.0),) * 3)
+    _decode_check(inp, 4, f"decode two-sided window page{page}", strict=False)
 
 
 @pytest.mark.parametrize("d,dv", [(64, 64), (96, 96), (192, 192), (256, 256), (192, 128)])
