@@ -141,7 +141,9 @@ typedef struct {
  * of one query head, looping over the visible KV tiles ("Native FP8 ... for Hopper", Design;
  * the method's steps: FP8 Q K^T, scale and mask, lazy-rescaled exp2 softmax with the 2^8 P
  * bias, E4M3 P, FP8 PV accumulated per KV tile and folded into fp32 O, v descale and 1/l at
- * the end). Works for fixed, varlen and paged K/V.
+ * the end). Works for fixed, varlen and paged K/V. FA8_ERR_INVALID also when the launch would
+ * need 2^31 or more workgroups (row blocks x query heads x batch, the batch x kv-head count
+ * rounded up to a multiple of 8 for varlen or seqused_k inputs).
  */
 fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);
 
