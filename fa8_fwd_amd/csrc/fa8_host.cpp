@@ -202,6 +202,8 @@ fa8::KParams make_kparams(const fa8_fwd_params* p) {
   k.causal = p->causal ? 1 : 0;
   k.out = p->out; k.o_bs = p->o_batch_stride; k.o_rs = p->o_row_stride; k.o_hs = p->o_head_stride;
   k.out_fp16 = p->out_dtype == FA8_OUT_FP16;
+  k.o_vec16 = aligned(p->out, 16) && p->o_row_stride % 8 == 0 && p->o_head_stride % 8 == 0 &&
+              (p->cu_seqlens_q || p->o_batch_stride % 8 == 0);
   k.lse = p->lse; k.l_bs = p->lse_batch_stride; k.l_hs = p->lse_head_stride; k.l_rs = p->lse_row_stride;
   k.sink = p->sink;
   return k;

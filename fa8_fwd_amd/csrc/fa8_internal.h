@@ -27,6 +27,7 @@ struct KParams {
   int32_t wl, wr;             // -1 = unbounded; wr = 0 when causal
   int32_t causal;
   void* out; int64_t o_bs, o_rs, o_hs; int32_t out_fp16;
+  int32_t o_vec16;            // out 16-byte aligned, its strides multiples of 8 elements
   float* lse; int64_t l_bs, l_hs, l_rs;
   float* o_part; float* lse_part; int32_t nsplit;
   int32_t nmb;                // row blocks per (batch, head) (decode) or per (batch, q head) (prefill)
@@ -44,6 +45,7 @@ struct CParams {
   int32_t nsplit, batch, max_sq, hq, dv;
   const int32_t* cu_q;
   void* out; int64_t o_bs, o_rs, o_hs; int32_t out_fp16;
+  int32_t o_vec16;            // out 16-byte aligned, its strides multiples of 8 elements
   float* lse; int64_t l_bs, l_hs, l_rs;
   const float* sink;          // [hq] sink logits or null
 };

@@ -229,7 +229,7 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 // Four consecutive outputs as 4 x 16-bit in 8 bytes.
-__device__ __forceinline__ void store4_half(void* dst, float a, float b, float c, float d, bool fp16) {
+__device__ __forceinline__ v2i pack4_half(float a, float b, float c, float d, bool fp16) {
   uint32_t lo, hi;
   if (fp16) {
     lo = f16_bits(a) | (f16_bits(b) << 16);
@@ -238,8 +238,11 @@ __device__ __forceinline__ void store4_half(void* dst, float a, float b, float c
     lo = bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
     hi = bf16_rne_bits(c) | (bf16_rne_bits(d) << 16);
   }
-  v2i v = {(int)lo, (int)hi};
-  *reinterpret_cast<v2i*>(dst) = v;
+  return (v2i){(int)lo, (int)hi};
+}
+
+__device__ __forceinline__ void store4_half(void* dst, float a, float b, float c, float d, bool fp16) {
+  *reinterpret_cast<v2i*>(dst) = pack4_half(a, b, c, d, fp16);
 }
 
 __device__ __forceinline__ float load_descale(const float* p, int64_t sb, int64_t sh, int b, int kvh) {
@@ -584,12 +587,16 @@ __device__ __forceinline__ void attn_tile16(const FA8_LDS uint8_t* kt, const FA8
 // offset as P: the stored max m rises to z2 = z log2 e when z2 is larger (alpha = 2^(m - m')
 // rescales l and O; every term stays below 2^8), then l += 2^(z2 - m' + 8). Split partials
 // leave the sink to the combine.
-template <int DV, bool SPLIT>
-__device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[DV / 32], float m_run, float l_tot,
-                                          float dvs, int hgrp, int b, int q0, int qi, int qh, int split,
-                                          float bias = kBias) {
-  constexpr int NB = DV / 32;
-  const float z2 = (!SPLIT && p.sink) ? p.sink[qh] * kLog2e : kNegInf;
+// Output scale and LSE of one row at the end of its key range: O = O_acc * dvs / l,
+// LSE = ln 2 * (m + log2 l - bias). With a sink logit z (when with_sink), the stored max is
+// first raised to z log2 e if that is larger, and the sink's term 2^(z log2 e - m + bias)
+// joins l; a row with no visible key and no sink gets O = 0 and LSE = -inf.
+struct RowScale {
+  float inv, lse;
+};
+__device__ __forceinline__ RowScale row_scale(const KParams& p, bool with_sink, int qh, float m_run, float l_tot,
+                                              float dvs, float bias) {
+  const float z2 = (with_sink && p.sink) ? p.sink[qh] * kLog2e : kNegInf;
   if (z2 != kNegInf) {
     const float mf = fmaxf(m_run, z2);
     const float a = (m_run == kNegInf) ? 0.0f : fast_exp2(m_run - mf);
@@ -598,8 +605,59 @@ __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[D
     m_run = mf;
   }
   const bool nonempty = l_tot > 0.0f;
-  const float inv = nonempty ? dvs / l_tot : 0.0f;
-  const float lse = nonempty ? (m_run + __log2f(l_tot) - bias) * kLn2 : kNegInf;
+  return {nonempty ? dvs / l_tot : 0.0f, nonempty ? (m_run + __log2f(l_tot) - bias) * kLn2 : kNegInf};
+}
+
+// Final output of one wave's 32 rows for DV in {64, 128, 256} when the output allows 16-byte
+// stores: the MFMA layout leaves each lane 4-column pieces of its row, so a direct store writes
+// 8 bytes into each of 32 rows per instruction. Instead the wave stages its rows in LDS
+// (`stage`: 32 rows x DV halves, its own region; every 16-byte chunk c of row r at chunk
+// c ^ (r mod DV/8), which spreads both the writes and the row reads over the banks) and writes
+// whole rows with 16-byte lanes. Rows past row_last are staged but not stored.
+template <int DV>
+__device__ __forceinline__ void store_rows_staged(const KParams& p, const v16f (&oacc)[DV / 32], float inv, int lane,
+                                                  int b, int q0, int row0, int row_last, int qh,
+                                                  FA8_LDS uint8_t* stage) {
+  constexpr int NB = DV / 32;
+  constexpr int CPR = DV / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  static_assert(CPR * RPI == 64 && (CPR & (CPR - 1)) == 0, "rows must split into 16-byte lanes");
+  const int hgrp = lane >> 5, lrow = lane & 31;
+  const bool fp16 = p.out_fp16 != 0;
+  // lane (row lrow, half hgrp) holds columns 32n + 8q4 + 4hgrp .. +3: half hgrp of chunk 4n + q4
+#pragma unroll
+  for (int n = 0; n < NB; n++)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; q4++) {
+      const int c = 4 * n + q4;
+      const int pos = lrow * (2 * DV) + ((c ^ (lrow & (CPR - 1))) << 4) + 8 * hgrp;
+      *(FA8_LDS v2i*)(stage + pos) = pack4_half(oacc[n][4 * q4] * inv, oacc[n][4 * q4 + 1] * inv,
+                                                oacc[n][4 * q4 + 2] * inv, oacc[n][4 * q4 + 3] * inv, fp16);
+    }
+  // the reads below take chunks other lanes of this wave wrote: the wave's LDS operations are
+  // performed in order, and the fence keeps the compiler from moving a read above a write
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int rr = lane / CPR, c = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; i++) {
+    const int r = RPI * i + rr;
+    const v4i x = *(const FA8_LDS v4i*)(stage + r * (2 * DV) + ((c ^ (r & (CPR - 1))) << 4));
+    const int qi = row0 + r;
+    if (qi <= row_last) {
+      const int64_t off = (p.cu_q ? (int64_t)(q0 + qi) * p.o_rs : (int64_t)b * p.o_bs + (int64_t)qi * p.o_rs) +
+                          (int64_t)qh * p.o_hs + 8 * c;
+      *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(p.out) + off) = x;
+    }
+  }
+}
+
+template <int DV, bool SPLIT>
+__device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[DV / 32], float m_run, float l_tot,
+                                          float dvs, int hgrp, int b, int q0, int qi, int qh, int split,
+                                          float bias = kBias) {
+  constexpr int NB = DV / 32;
+  const RowScale rsc = row_scale(p, !SPLIT, qh, m_run, l_tot, dvs, bias);
+  const float inv = rsc.inv, lse = rsc.lse;
   if constexpr (SPLIT) {
     const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi) * p.hq + qh;
     float* orow = p.o_part + prow * DV;
@@ -808,6 +866,21 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   }
 
   const float l_tot = l_run;   // the MFMA row sums already cover both lanes of a row
+  if constexpr (DV == 64 || DV == 128 || DV == 256) {
+    static_assert(NW * 32 * 2 * DV <= 2 * STAGE, "the staged output must fit in the two tile stages");
+    if (p.o_vec16) {
+      // the loop ended on a barrier with no copy in flight: the tile stages are free
+      const RowScale rsc = row_scale(p, true, qh, m_run, l_tot, dvs, kBias);
+      if (valid && hgrp == 0 && p.lse) {
+        const int64_t loff = p.cu_q ? (int64_t)qh * p.l_hs + (int64_t)(si.q0 + qi) * p.l_rs
+                                    : (int64_t)b * p.l_bs + (int64_t)qh * p.l_hs + (int64_t)qi * p.l_rs;
+        p.lse[loff] = rsc.lse;
+      }
+      store_rows_staged<DV>(p, oacc, rsc.inv, lane, b, si.q0, rb0 + wave * 32, rb1, qh,
+                            (FA8_LDS uint8_t*)smem + wave * (32 * 2 * DV));
+      return;
+    }
+  }
   if (!valid) return;
   store_row<DV, false>(p, oacc, m_run, l_tot, dvs, hgrp, b, si.q0, qi, qh, 0);
 }

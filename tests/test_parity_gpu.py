@@ -116,6 +116,25 @@ def test_prefill_paged_equals_contiguous_bitwise():
     assert np.array_equal(got, got2) and np.array_equal(glse, glse2)
 
 
+@pytest.mark.parametrize("d,dv", [(64, 64), (128, 128), (256, 256), (192, 128)])
+def test_prefill_output_layouts_bitwise(d, dv):
+    # the output written through 16-byte row stores (16-byte aligned output, strides multiples of
+    # 8 elements) equals the output written into a padded view (head stride dv + 4 elements,
+    # 8-byte aligned) bit for bit, and the oracle check holds for the padded one too
+    inp = gen.make_dense(60 + d, 2, 203, 331, 4, 2, d, dv, causal=True)
+    q, k, v, kw = tensors(inp)
+    a = torch.empty((2, 203, 4, dv), dtype=torch.bfloat16, device=q.device)
+    big = torch.zeros((2, 203, 4, dv + 4), dtype=torch.bfloat16, device=q.device)
+    b = big[..., 4:]
+    la = binding.prefill(q, k, v, out=a, return_lse=True, **kw)[1]
+    lb = binding.prefill(q, k, v, out=b, return_lse=True, **kw)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    assert torch.all(big[..., :4] == 0)     # nothing written outside the view
+    _check(inp, b.float().cpu().numpy(), lb.cpu().numpy(), f"prefill d{d} dv{dv} padded output",
+           tile_n=prefill_tile(d, dv))
+
+
 def test_prefill_deterministic():
     inp = gen.make_dense(8, 1, 256, 256, 4, 4, 128, 128, causal=True)
     a, la = run_prefill(inp)
