@@ -1225,6 +1225,16 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_mx_kernel(const KParams p)
     __syncthreads();
   }
 
+  static_assert(NW * 32 * 2 * DV <= 2 * STAGE, "the staged output must fit in the two tile stages");
+  if (p.o_vec16) {
+    // the loop ended on a barrier with no copy or scale store in flight: the stages are free
+    const RowScale rsc = row_scale(p, true, qh, m_run, l_run, 1.0f, 0.0f);
+    if (valid && hgrp == 0 && p.lse)
+      p.lse[(int64_t)b * p.l_bs + (int64_t)qh * p.l_hs + (int64_t)qi * p.l_rs] = rsc.lse;
+    store_rows_staged<DV>(p, oacc, rsc.inv, lane, b, 0, rb0 + wave * 32, rb1, qh,
+                          (FA8_LDS uint8_t*)smem + wave * (32 * 2 * DV));
+    return;
+  }
   if (!valid) return;
   store_row<DV, false>(p, oacc, m_run, l_run, 1.0f, hgrp, b, 0, qi, qh, 0, 0.0f);
 }

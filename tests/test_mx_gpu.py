@@ -150,3 +150,20 @@ def test_mx_prefill_long_causal_sampled_rows():
     assert lerr.max() <= LSE_BOUND, f"long causal LSE err {lerr.max()}"
     print(f"long causal: max abs err {err.max():.4g}, {frac:.3%} beyond 2e-2, LSE max err {lerr.max():.3g}",
           flush=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mx_prefill_output_layouts_bitwise(d):
+    # 16-byte row stores (aligned output) and the direct store (padded view, head stride d + 4)
+    # give the same bytes
+    inp = gen.make_mx(23 + d, 2, 203, 331, 4, 2, d, d, causal=True)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    qs, ks, vs = to_dev(inp.q_mx), to_dev(inp.k_mx), to_dev(inp.v_mx)
+    a = torch.empty((2, 203, 4, d), dtype=torch.bfloat16, device=q.device)
+    big = torch.zeros((2, 203, 4, d + 4), dtype=torch.bfloat16, device=q.device)
+    b = big[..., 4:]
+    la = binding.prefill_mx(q, k, v, qs, ks, vs, causal=True, out=a, return_lse=True)[1]
+    lb = binding.prefill_mx(q, k, v, qs, ks, vs, causal=True, out=b, return_lse=True)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)
+    assert torch.all(big[..., :4] == 0)
