@@ -18,6 +18,7 @@ FA8_OUT_BF16, FA8_OUT_FP16 = 0, 1
 SPLIT_GRANULE = 64
 DECODE_BLOCK_ROWS = 32
 MAX_SPLITS = 256
+DECODE_AUTO, DECODE_PER_HEAD, DECODE_HEAD_GROUP = -1, 0, 1
 
 
 class FA8Error(RuntimeError):
@@ -102,6 +103,8 @@ def load():
     lib.fa8_fwd_prefill.argtypes = [P, vp]
     lib.fa8_fwd_prefill_mx.argtypes = [P, ctypes.POINTER(MXScales), vp]
     lib.fa8_fwd_decode_splitkv.argtypes = [P, i32, vp, vp, vp]
+    lib.fa8_fwd_decode_splitkv_ex.argtypes = [P, i32, i32, vp, vp, vp]
+    lib.fa8_fwd_decode_splitkv_ex.restype = ctypes.c_int
     lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, vp]
     lib.fa8_check_params.argtypes = [P, i32]
     QP = ctypes.POINTER(QuantParams)
@@ -115,6 +118,8 @@ def load():
     lib.fa8_decode_num_splits.restype = i32
     lib.fa8_decode_plan.argtypes = [P, i32, ctypes.POINTER(DecodePlan)]
     lib.fa8_decode_plan.restype = ctypes.c_int
+    lib.fa8_decode_plan_ex.argtypes = [P, i32, i32, ctypes.POINTER(DecodePlan)]
+    lib.fa8_decode_plan_ex.restype = ctypes.c_int
     lib.fa8_decode_num_splits_for.argtypes = [P, i32]
     lib.fa8_decode_num_splits_for.restype = i32
     lib.fa8_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -343,13 +348,13 @@ def decode_num_splits_for(q, k, v, *, cu_count: int = 0, **kw) -> int:
     return int(load().fa8_decode_num_splits_for(ctypes.byref(p), cu_count))
 
 
-def decode_plan(q, k, v, *, num_splits: int, **kw) -> dict:
-    """How fa8_fwd_decode_splitkv computes this problem (fa8_decode_plan): kernel, block_keys,
-    key_groups, heads_per_workgroup, workgroups."""
+def decode_plan(q, k, v, *, num_splits: int, kernel: int = DECODE_AUTO, **kw) -> dict:
+    """How fa8_fwd_decode_splitkv_ex computes this problem (fa8_decode_plan_ex): kernel,
+    block_keys, key_groups, heads_per_workgroup, workgroups."""
     p = _params(q, k, v, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
                 kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), None, None, None, 0.0, False, -1, -1)
     info = DecodePlan()
-    _check(load().fa8_decode_plan(ctypes.byref(p), num_splits, ctypes.byref(info)))
+    _check(load().fa8_decode_plan_ex(ctypes.byref(p), num_splits, kernel, ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in DecodePlan._fields_}
 
 
@@ -360,9 +365,10 @@ def decode_workspace_bytes(num_splits: int, batch: int, max_seqlen_q: int, heads
 def decode_splitkv(q, k, v, *, num_splits: int, o_partial=None, lse_partial=None, cu_seqlens_q=None,
                    cu_seqlens_k=None, seqused_k=None, block_table=None, max_seqlen_q=None, max_seqlen_k=None,
                    q_descale=None, k_descale=None, v_descale=None, softmax_scale: float = 0.0, causal: bool = False,
-                   window_left: int = -1, window_right: int = -1, stream=None):
-    """Split-KV partial pass (fa8_fwd_decode_splitkv). Returns (o_partial, lse_partial) with shapes
-    [S, B, max_seqlen_q, Hq, dv] and [S, B, max_seqlen_q, Hq] (fp32)."""
+                   window_left: int = -1, window_right: int = -1, kernel: int = DECODE_AUTO, stream=None):
+    """Split-KV partial pass (fa8_fwd_decode_splitkv_ex; kernel: DECODE_AUTO, DECODE_PER_HEAD or
+    DECODE_HEAD_GROUP). Returns (o_partial, lse_partial) with shapes [S, B, max_seqlen_q, Hq, dv]
+    and [S, B, max_seqlen_q, Hq] (fp32)."""
     lib = load()
     p = _params(q, k, v, cu_seqlens_q, cu_seqlens_k, seqused_k, block_table, max_seqlen_q, max_seqlen_k,
                 q_descale, k_descale, v_descale, softmax_scale, causal, window_left, window_right)
@@ -375,7 +381,8 @@ def decode_splitkv(q, k, v, *, num_splits: int, o_partial=None, lse_partial=None
         raise FA8Error(FA8_ERR_INVALID, "partial buffers too small")
     if not (o_partial.is_contiguous() and lse_partial.is_contiguous()):
         raise FA8Error(FA8_ERR_INVALID, "partial buffers must be contiguous")
-    _check(lib.fa8_fwd_decode_splitkv(ctypes.byref(p), S, o_partial.data_ptr(), lse_partial.data_ptr(), _stream(stream)))
+    _check(lib.fa8_fwd_decode_splitkv_ex(ctypes.byref(p), S, kernel, o_partial.data_ptr(), lse_partial.data_ptr(),
+                                         _stream(stream)))
     return o_partial, lse_partial
 
 
@@ -404,7 +411,8 @@ def combine(o_partial, lse_partial, *, batch: int, max_seqlen_q: int, heads_q: i
 
 
 def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=torch.bfloat16, return_lse=False,
-           workspace: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None, stream=None, **kw):
+           workspace: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None, kernel: int = DECODE_AUTO,
+           stream=None, **kw):
     """Split-KV decode followed by the combine. num_splits=None uses fa8_decode_num_splits_for; the
     sink (optional [heads_q] fp32 logits) enters in the combine."""
     cu_q = kw.get("cu_seqlens_q")
@@ -420,7 +428,8 @@ def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=tor
         flat = workspace.view(torch.float32).reshape(-1)
         op = flat[:n_o].view(S, B, SQ, HQ, DV)
         lp = flat[off_l:off_l + n_l].view(S, B, SQ, HQ)
-    op, lp = decode_splitkv(q, k, v, num_splits=num_splits, o_partial=op, lse_partial=lp, stream=stream, **kw)
+    op, lp = decode_splitkv(q, k, v, num_splits=num_splits, o_partial=op, lse_partial=lp, kernel=kernel, stream=stream,
+                            **kw)
     varlen = cu_q is not None
     if out is None:
         out, lse = _alloc_out(q, DV, out_dtype, varlen, return_lse, B, HQ, SQ)

@@ -47,12 +47,25 @@ int ilog2_exact(int x) {
 }
 
 constexpr int64_t kMaxLen = (int64_t)1 << 30;
+// A launch's grid may hold at most 2^32 - 1 threads along x: 2^24 workgroups of 256 threads
+// (prefill), 2^26 of 64 (decode).
+constexpr int64_t kMaxPrefillGrid = (int64_t)1 << 24;
+constexpr int64_t kMaxDecodeGridX = (int64_t)1 << 26;
 
 fa8_status check_descale(const fa8_descale& ds, const char* name) {
   if (!ds.ptr) return FA8_OK;
   if (!aligned(ds.ptr, 4)) return fail(FA8_ERR_INVALID, "%s_descale pointer is not 4-byte aligned", name);
   if (ds.stride_b < 0 || ds.stride_h < 0) return fail(FA8_ERR_INVALID, "%s_descale strides must be >= 0", name);
   return FA8_OK;
+}
+
+// Workgroups of a prefill launch (fa8::prefill_grid of the kernel parameters the launch builds).
+int64_t prefill_workgroups(const fa8_fwd_params* p) {
+  const int64_t nmb = ((int64_t)p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
+  const int64_t g = p->heads_kv > 0 ? p->heads_q / p->heads_kv : 0;
+  if (p->cu_seqlens_q || p->cu_seqlens_k || p->seqused_k)
+    return (int64_t)8 * (((int64_t)p->batch * p->heads_kv + 7) / 8) * nmb * g;
+  return nmb * p->heads_q * p->batch;
 }
 
 // Validation shared by prefill (num_splits == 0) and decode (num_splits >= 1).
@@ -111,6 +124,9 @@ fa8_status validate(const fa8_fwd_params* p, int32_t num_splits) {
     for (int64_t s : so)
       if (s < 0 || s % 4 != 0) return fail(FA8_ERR_INVALID, "out strides must be non-negative multiples of 4");
     if (p->lse && !aligned(p->lse, 4)) return fail(FA8_ERR_INVALID, "lse must be 4-byte aligned");
+    if (prefill_workgroups(p) >= kMaxPrefillGrid)
+      return fail(FA8_ERR_INVALID, "prefill needs %lld workgroups of 256 threads, more than one launch can hold (2^24)",
+                  (long long)prefill_workgroups(p));
   } else {
     const int64_t rows = (int64_t)p->max_seqlen_q * (p->heads_q / p->heads_kv);
     if (rows > kMaxLen) return fail(FA8_ERR_INVALID, "too many packed decode rows");
@@ -128,6 +144,8 @@ bool validate_env() {
   return e && e[0] == '1';
 }
 
+// The copies below run after everything already enqueued on the caller's stream (the index
+// arrays may have just been written there): the stream is synchronized first.
 template <typename T>
 bool copy_down(std::vector<T>& dst, const T* src, size_t n) {
   dst.resize(n);
@@ -135,7 +153,9 @@ bool copy_down(std::vector<T>& dst, const T* src, size_t n) {
   return hipMemcpy(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost) == hipSuccess;
 }
 
-fa8_status validate_device_data(const fa8_fwd_params* p) {
+fa8_status validate_device_data(const fa8_fwd_params* p, void* stream) {
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return fail(FA8_ERR_HIP, "FA8_VALIDATE: cannot synchronize the stream");
   const int B = p->batch;
   std::vector<int32_t> cuq, cuk, used, table;
   if (p->cu_seqlens_q) {
@@ -206,6 +226,7 @@ fa8::KParams make_kparams(const fa8_fwd_params* p) {
               (p->cu_seqlens_q || p->o_batch_stride % 8 == 0);
   k.lse = p->lse; k.l_bs = p->lse_batch_stride; k.l_hs = p->lse_head_stride; k.l_rs = p->lse_row_stride;
   k.sink = p->sink;
+  k.decode_kernel = -1;
   return k;
 }
 
@@ -222,39 +243,59 @@ fa8_status fa8_check_params(const fa8_fwd_params* p, int32_t num_splits) {
   return st == FA8_OK ? ok() : st;
 }
 
-int32_t fa8_decode_num_splits(int32_t batch, int32_t heads_kv, int32_t max_seqlen_k, int32_t cu_count) {
+}  // extern "C"
+
+namespace {
+// Split count for `units` one-wave workgroups per split: about `waves_per_cu` waves per compute
+// unit, without splits shorter than four granules, within 1 .. FA8_MAX_SPLITS.
+int32_t splits_for(int64_t units, int32_t max_seqlen_k, int32_t cu_count, int waves_per_cu) {
   if (cu_count <= 0) cu_count = 256;
-  if (batch <= 0 || heads_kv <= 0 || max_seqlen_k <= 0) return 1;
-  const int64_t units = (int64_t)batch * heads_kv;
-  const int64_t target = (int64_t)cu_count * 8;               // workgroups to keep every CU busy
+  units = std::max<int64_t>(1, units);
+  const int64_t target = (int64_t)cu_count * waves_per_cu;
   const int64_t granules = ((int64_t)max_seqlen_k + FA8_SPLIT_GRANULE - 1) / FA8_SPLIT_GRANULE;
   int64_t s = (target + units - 1) / units;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, granules / 4));  // at least ~4 granules per split
-  s = std::max<int64_t>(1, std::min<int64_t>(s, FA8_MAX_SPLITS));
-  return (int32_t)s;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, granules / 4));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, FA8_MAX_SPLITS));
+}
+// Waves per compute unit the split heuristic aims at: several-heads kernel about one per SIMD
+// (more concurrent streams measured slower), per-head kernel about four per SIMD (measured best
+// at the paged GQA decode shape).
+constexpr int kHeadsWavesPerCu = 4, kPerHeadWavesPerCu = 16;
+
+int decode_kernel_for(const fa8::KParams& k, const fa8_fwd_params* p, int32_t requested, fa8_status* st) {
+  *st = FA8_OK;
+  if (requested < -1 || requested > 1) {
+    *st = fail(FA8_ERR_INVALID, "decode kernel %d is not one of -1, 0, 1", requested);
+    return 0;
+  }
+  if (requested == 1 && !fa8::decode_heads_applicable(k, p->d, p->dv)) {
+    *st = fail(FA8_ERR_UNSUPPORTED, "the several-heads decode kernel cannot take this problem");
+    return 0;
+  }
+  return requested;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t fa8_decode_num_splits(int32_t batch, int32_t heads_kv, int32_t max_seqlen_k, int32_t cu_count) {
+  if (batch <= 0 || heads_kv <= 0 || max_seqlen_k <= 0) return 1;
+  return splits_for((int64_t)batch * heads_kv, max_seqlen_k, cu_count, kPerHeadWavesPerCu);
 }
 
 int32_t fa8_decode_num_splits_for(const fa8_fwd_params* p, int32_t cu_count) {
   if (!p || validate(p, 1) != FA8_OK) return 1;
-  if (cu_count <= 0) cu_count = 256;
   if (p->batch <= 0 || p->heads_kv <= 0 || p->max_seqlen_k <= 0 || p->max_seqlen_q <= 0) return 1;
   fa8::KParams k = make_kparams(p);
   const int64_t rows = (int64_t)p->max_seqlen_q * k.g;
   k.nmb = (int32_t)((rows + fa8::kDecodeRows - 1) / fa8::kDecodeRows);
-  const int64_t units = std::max<int64_t>(1, fa8::decode_units_per_split(k, p->d, p->dv));
-  // one-wave workgroups. Several-heads kernel: about one wave per SIMD (more concurrent streams
-  // measured slower); per-head kernel: about four per SIMD (measured best at the paged GQA
-  // decode shape)
   const bool heads = fa8::decode_heads_choice(k, p->d, p->dv) != 0;
-  const int64_t target = (int64_t)cu_count * (heads ? 4 : 16);
-  const int64_t granules = ((int64_t)p->max_seqlen_k + FA8_SPLIT_GRANULE - 1) / FA8_SPLIT_GRANULE;
-  int64_t s = (target + units - 1) / units;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, granules / 4));
-  s = std::max<int64_t>(1, std::min<int64_t>(s, FA8_MAX_SPLITS));
-  return (int32_t)s;
+  return splits_for(fa8::decode_units_per_split(k, p->d, p->dv), p->max_seqlen_k, cu_count,
+                    heads ? kHeadsWavesPerCu : kPerHeadWavesPerCu);
 }
 
-fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_decode_plan_info* info) {
+fa8_status fa8_decode_plan_ex(const fa8_fwd_params* p, int32_t num_splits, int32_t kernel,
+                              fa8_decode_plan_info* info) {
   if (!info) return fail(FA8_ERR_INVALID, "info must be non-NULL");
   if (num_splits < 1) return fail(FA8_ERR_INVALID, "num_splits must be >= 1 (got %d)", num_splits);
   fa8_status st = validate(p, num_splits);
@@ -263,6 +304,8 @@ fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_deco
   k.nsplit = num_splits;
   const int64_t rows = (int64_t)p->max_seqlen_q * k.g;
   k.nmb = (int32_t)((rows + fa8::kDecodeRows - 1) / fa8::kDecodeRows);
+  k.decode_kernel = decode_kernel_for(k, p, kernel, &st);
+  if (st != FA8_OK) return st;
   const int hpw = fa8::decode_heads_choice(k, p->d, p->dv);
   if (hpw) {
     info->kernel = 1;
@@ -279,6 +322,10 @@ fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_deco
   return ok();
 }
 
+fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_decode_plan_info* info) {
+  return fa8_decode_plan_ex(p, num_splits, -1, info);
+}
+
 size_t fa8_decode_workspace_bytes(int32_t num_splits, int32_t batch, int32_t max_seqlen_q, int32_t heads_q,
                                   int32_t dv) {
   if (num_splits < 0 || batch < 0 || max_seqlen_q < 0 || heads_q < 0 || dv < 0) return 0;
@@ -293,13 +340,13 @@ fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream) {
   fa8_status st = validate(p, 0);
   if (st != FA8_OK) return st;
   if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
-  if (validate_env() && (st = validate_device_data(p)) != FA8_OK) return st;
+  if (validate_env() && (st = validate_device_data(p, stream)) != FA8_OK) return st;
   fa8::KParams k = make_kparams(p);
   k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
   // lengths read on the device: deal the (batch, kv head) groups to the XCDs round-robin
   if (p->cu_seqlens_q || p->cu_seqlens_k || p->seqused_k)
     k.bk8 = (int32_t)(((int64_t)p->batch * p->heads_kv + 7) / 8);
-  if (fa8::prefill_grid(k) >= ((int64_t)1 << 31)) return fail(FA8_ERR_INVALID, "prefill grid too large");
+  if (fa8::prefill_grid(k) != prefill_workgroups(p)) return fail(FA8_ERR_INVALID, "internal: prefill grid mismatch");
   hipError_t e = fa8::launch_prefill(k, p->d, p->dv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA8_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -332,7 +379,7 @@ fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, v
   if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
   fa8::KParams k = make_kparams(p);
   k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
-  if (fa8::prefill_grid(k) >= ((int64_t)1 << 31)) return fail(FA8_ERR_INVALID, "prefill grid too large");
+  if (fa8::prefill_grid(k) != prefill_workgroups(p)) return fail(FA8_ERR_INVALID, "internal: prefill grid mismatch");
   k.q_mx = s->q; k.qmx_bs = s->q_batch_stride; k.qmx_rs = s->q_row_stride; k.qmx_hs = s->q_head_stride;
   k.k_mx = s->k; k.kmx_bs = s->k_batch_stride; k.kmx_rs = s->k_row_stride; k.kmx_hs = s->k_head_stride;
   k.v_mx = s->v; k.vmx_bs = s->v_batch_stride; k.vmx_ts = s->v_block_stride; k.vmx_hs = s->v_head_stride;
@@ -341,26 +388,33 @@ fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, v
   return ok();
 }
 
-fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, float* o_partial, float* lse_partial,
-                                  void* stream) {
+fa8_status fa8_fwd_decode_splitkv_ex(const fa8_fwd_params* p, int32_t num_splits, int32_t kernel, float* o_partial,
+                                     float* lse_partial, void* stream) {
   if (num_splits < 1) return fail(FA8_ERR_INVALID, "num_splits must be >= 1 (got %d)", num_splits);
   fa8_status st = validate(p, num_splits);
+  if (st != FA8_OK) return st;
+  fa8::KParams k = make_kparams(p);
+  k.decode_kernel = decode_kernel_for(k, p, kernel, &st);
   if (st != FA8_OK) return st;
   if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
   if (!o_partial || !lse_partial) return fail(FA8_ERR_INVALID, "o_partial and lse_partial must be non-NULL");
   if (!aligned(o_partial, 16) || !aligned(lse_partial, 4))
     return fail(FA8_ERR_INVALID, "o_partial must be 16-byte aligned and lse_partial 4-byte aligned");
-  if (validate_env() && (st = validate_device_data(p)) != FA8_OK) return st;
-  fa8::KParams k = make_kparams(p);
+  if (validate_env() && (st = validate_device_data(p, stream)) != FA8_OK) return st;
   k.o_part = o_partial;
   k.lse_part = lse_partial;
   k.nsplit = num_splits;
   const int64_t rows = (int64_t)p->max_seqlen_q * k.g;
   k.nmb = (int32_t)((rows + fa8::kDecodeRows - 1) / fa8::kDecodeRows);
-  if ((int64_t)k.nmb * p->heads_kv >= ((int64_t)1 << 31)) return fail(FA8_ERR_INVALID, "decode grid too large");
+  if ((int64_t)k.nmb * p->heads_kv >= kMaxDecodeGridX) return fail(FA8_ERR_INVALID, "decode grid too large");
   hipError_t e = fa8::launch_decode(k, p->d, p->dv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA8_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, float* o_partial, float* lse_partial,
+                                  void* stream) {
+  return fa8_fwd_decode_splitkv_ex(p, num_splits, -1, o_partial, lse_partial, stream);
 }
 
 fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t num_splits, int32_t batch,

@@ -33,6 +33,7 @@ struct KParams {
   int32_t nmb;                // row blocks per (batch, head) (decode) or per (batch, q head) (prefill)
   int32_t bk8;                // prefill with per-sequence lengths: ceil(batch * hkv / 8), else 0
   const float* sink;          // [hq] sink logits or null (prefill finalize only)
+  int32_t decode_kernel;      // -1: the library's choice; 0: per-head kernel; 1: several heads per wave
   // MXFP8 block scales (E8M0 bytes; strides in bytes), MX prefill only
   const uint8_t* q_mx; int64_t qmx_bs, qmx_rs, qmx_hs;
   const uint8_t* k_mx; int64_t kmx_bs, kmx_rs, kmx_hs;
@@ -74,7 +75,9 @@ inline int64_t prefill_grid(const KParams& k) {
 constexpr int kDecodeRows = 32;
 constexpr int kKvTile = 64;
 
-// kv heads per wave of the several-heads decode kernel, or 0 when the per-head kernel is used.
+// kv heads per wave the several-heads decode kernel would use for this problem, or 0 when it
+// cannot take it; and the same subject to kp.decode_kernel (0 when the per-head kernel is used).
+int decode_heads_applicable(const KParams& kp, int d, int dv);
 int decode_heads_choice(const KParams& kp, int d, int dv);
 // Workgroups per split of the decode kernel launch_decode picks.
 int decode_units_per_split(const KParams& kp, int d, int dv);

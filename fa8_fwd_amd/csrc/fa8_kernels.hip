@@ -30,7 +30,6 @@
 //    the rows that one LDS read instruction touches fall in distinct banks.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <type_traits>
 
@@ -2132,9 +2131,7 @@ hipError_t launch_prefill_mx(const KParams& kp, int d, int dv, hipStream_t strea
 // in memory (head stride == head dim), 2 or 4 kv heads whose Sq * g rows fit one 16-row block,
 // and (paged) pages holding at least the rows of one 64-lane load. (Eight heads per wave, two
 // row blocks, measured slower: fewer waves and register spills.)
-int decode_heads_choice(const KParams& kp, int d, int dv) {
-  const char* env = getenv("FA8_DECODE_KERNEL");
-  if (env && env[0] == 'l') return 0;   // "lanes": force the per-head decode kernel
+int decode_heads_applicable(const KParams& kp, int d, int dv) {
   if (!((d == 64 && dv == 64) || (d == 128 && dv == 128))) return 0;
   if (kp.k_hs != d || kp.v_hs != dv) return 0;
   const int64_t rp = (int64_t)kp.max_sq * kp.g;
@@ -2146,6 +2143,9 @@ int decode_heads_choice(const KParams& kp, int d, int dv) {
     return hpw;
   }
   return 0;
+}
+int decode_heads_choice(const KParams& kp, int d, int dv) {
+  return kp.decode_kernel == 0 ? 0 : decode_heads_applicable(kp, d, dv);
 }
 
 template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE>

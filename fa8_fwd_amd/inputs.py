@@ -228,6 +228,46 @@ def _mx_blocks(x: torch.Tensor, axis: int):
     return codes.numpy(), scales.numpy()
 
 
+def _mx_blocks_random(x: torch.Tensor, axis: int, gen: torch.Generator, lo: int, hi: int):
+    """MXFP8 encoding of float32 x in blocks of 32 along `axis` with a random shared exponent per
+    block: X uniform in [lo, hi], raised where needed to ceil(log2(amax / 448)) so that no element
+    exceeds 448; elements x / 2^X cast to E4M3 (round to nearest even). The dequantized values are
+    x up to the E4M3 rounding, while the element magnitudes and scale bytes vary by up to
+    2^(hi - lo) from block to block."""
+    x = x.movedim(axis, -1)
+    n = x.shape[-1]
+    nb = (n + 31) // 32
+    pad = torch.zeros(x.shape[:-1] + (nb * 32,), dtype=torch.float32)
+    pad[..., :n] = x
+    blk = pad.reshape(x.shape[:-1] + (nb, 32))
+    amax = blk.abs().amax(dim=-1)
+    need = torch.where(amax > 0, torch.ceil(torch.log2(amax / 448.0)), torch.full_like(amax, -127.0))
+    e = torch.randint(lo, hi + 1, amax.shape, generator=gen).to(torch.float32)
+    e = torch.maximum(e, need).clamp(-127, 127)
+    codes = (blk / torch.exp2(e)[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    codes = codes.reshape(pad.shape)[..., :n].movedim(-1, axis).contiguous()
+    scales = (e + 127).to(torch.uint8).movedim(-1, axis).contiguous()
+    return codes.numpy(), scales.numpy()
+
+
+def make_mx_random_exponents(seed: int, batch: int, sq: int, sk: int, heads_q: int, heads_kv: int, d: int,
+                             dv: int, lo: int = -5, hi: int = 5, causal: bool = False, window_left: int = -1,
+                             out_dtype: str = "bf16") -> AttnInputs:
+    """Like make_mx, but every block takes a random shared exponent in [lo, hi] (at least the one
+    its largest element needs): the attention values are N(0,1) data as in make_mx, while the
+    E4M3 elements and E8M0 scale bytes spread over 2^(hi - lo) from block to block. Draw order:
+    Q, K, V values, then the exponents of Q, K, V blocks."""
+    g = torch.Generator().manual_seed(seed)
+    qf = torch.randn((batch, sq, heads_q, d), generator=g, dtype=torch.float32)
+    kf = torch.randn((batch, sk, heads_kv, d), generator=g, dtype=torch.float32)
+    vf = torch.randn((batch, sk, heads_kv, dv), generator=g, dtype=torch.float32)
+    q, qs = _mx_blocks_random(qf, -1, g, lo, hi)
+    k, ks = _mx_blocks_random(kf, -1, g, lo, hi)
+    v, vs = _mx_blocks_random(vf, 1, g, lo, hi)
+    return AttnInputs(batch, heads_q, heads_kv, d, dv, q, k, v, sq, sk, causal=causal, window_left=window_left,
+                      out_dtype=out_dtype, name=f"mx_random_exponents_{lo}_{hi}", q_mx=qs, k_mx=ks, v_mx=vs)
+
+
 def make_mx(seed: int, batch: int, sq: int, sk: int, heads_q: int, heads_kv: int, d: int, dv: int,
             causal: bool = False, window_left: int = -1, window_right: int = -1, v_mean: float = 0.0,
             softmax_scale: float = 0.0, out_dtype: str = "bf16", name: str = "") -> AttnInputs:

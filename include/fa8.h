@@ -28,7 +28,8 @@
  *    sequence length above max_seqlen_q / max_seqlen_k, or cu_seqlens that are not
  *    nondecreasing. FA8_VALIDATE=1 checks what the ABI can see (lengths against the maxima,
  *    monotone cu_seqlens, non-negative page indices; the pool size is not an argument) on host
- *    copies and returns FA8_ERR_INVALID on a violation.
+ *    copies and returns FA8_ERR_INVALID on a violation; it first synchronizes `stream` (so that it
+ *    sees index arrays written there), which is why it cannot run under stream capture.
  */
 #ifndef FA8_H
 #define FA8_H
@@ -109,6 +110,11 @@ typedef struct {
  *   ("Native FP8 ... for Hopper", Supported); anything else is FA8_ERR_UNSUPPORTED.
  * Sizes: every dimension >= 0 (an empty problem launches nothing and returns FA8_OK); batch < 2^16;
  *   max_seqlen_q, max_seqlen_k < 2^30; heads < 2^16.
+ * Score precision: the scores S = Q K^T are computed by the FP8 matrix cores, whose dot products
+ *   carry an error up to about 2^-14 of sum_i |q_i k_i| (measured on gfx950, unscaled and
+ *   block-scaled operands alike); each scaled score, and so the LSE, carries that error times
+ *   softmax_scale * q_descale * k_descale. For inputs of ordinary magnitude (scores of a few
+ *   units) it is far below the E4M3 rounding of P; it grows with the magnitude of the products.
  */
 typedef struct {
   int32_t batch, heads_q, heads_kv, d, dv;
@@ -141,9 +147,11 @@ typedef struct {
  * of one query head, looping over the visible KV tiles ("Native FP8 ... for Hopper", Design;
  * the method's steps: FP8 Q K^T, scale and mask, lazy-rescaled exp2 softmax with the 2^8 P
  * bias, E4M3 P, FP8 PV accumulated per KV tile and folded into fp32 O, v descale and 1/l at
- * the end). Works for fixed, varlen and paged K/V. FA8_ERR_INVALID also when the launch would
- * need 2^31 or more workgroups (row blocks x query heads x batch, the batch x kv-head count
- * rounded up to a multiple of 8 for varlen or seqused_k inputs).
+ * the end). Works for fixed, varlen and paged K/V. KV tile: 128 keys when d + dv <= 256, else
+ * 64, counted from key 0 of the sequence; each tile is one step of the online softmax (row max,
+ * lazy rescale, P, PV from zero, fold into O). FA8_ERR_INVALID also when the launch would need
+ * 2^24 or more workgroups of 256 threads (ceil(max_seqlen_q / 128) x query heads x batch; for
+ * varlen or seqused_k inputs the batch x kv-head count is rounded up to a multiple of 8 first).
  */
 fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);
 
@@ -167,6 +175,24 @@ fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);
  */
 fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, float* o_partial,
                                   float* lse_partial, void* stream);
+
+/* Decode kernels fa8_fwd_decode_splitkv_ex can be asked for (fa8_decode_plan_info.kernel).
+ * AUTO is the library's choice (what fa8_fwd_decode_splitkv uses). PER_HEAD takes every problem.
+ * HEAD_GROUP (several kv heads per wave, whole token rows) takes (d, dv) = (64, 64) or
+ * (128, 128) with the heads of a token row adjacent in memory (head stride = head dim), at most
+ * 8 packed rows (max_seqlen_q x heads_q / heads_kv) per kv head, heads_kv a multiple of 2 and,
+ * when paged, pages of at least 1024 / (heads per wave x d) rows; other problems return
+ * FA8_ERR_UNSUPPORTED. Both compute the same partition and the same method; their blocking
+ * differs (fa8_decode_plan_ex), so results may differ in rounding. */
+typedef enum {
+  FA8_DECODE_AUTO = -1,
+  FA8_DECODE_PER_HEAD = 0,
+  FA8_DECODE_HEAD_GROUP = 1
+} fa8_decode_kernel;
+
+/* fa8_fwd_decode_splitkv with an explicit kernel choice (a fa8_decode_kernel value). */
+fa8_status fa8_fwd_decode_splitkv_ex(const fa8_fwd_params* p, int32_t num_splits, int32_t kernel,
+                                     float* o_partial, float* lse_partial, void* stream);
 
 /*
  * Merges split partials into the final output: LSE = log sum_s exp(LSE_s),
@@ -261,12 +287,18 @@ typedef struct {
 fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, void* stream);
 
 /* Runs the host-side validation of fa8_fwd_prefill (num_splits == 0) or of
- * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything. Needs no GPU. */
+ * fa8_fwd_decode_splitkv (num_splits >= 1) without launching anything, so that a caller can
+ * check a problem before graph capture. Needs no GPU. The checks are the interface limits the
+ * Hopper FP8 page states (Design and Supported: the (d, dv) set, E4M3 inputs, 0-d or
+ * (batch, kv_heads) descales, the 32-bit offsets inside a tile) plus this ABI's own layout rules
+ * above. */
 fa8_status fa8_check_params(const fa8_fwd_params* p, int32_t num_splits);
 
-/* Split count for fa8_fwd_decode_splitkv computed from host-side values only, so that it holds
- * under graph capture ("Native FP8 ... for Hopper", Design, Decode launches): enough (batch * heads_kv * splits) workgroups
- * to fill cu_count compute units, without splits shorter than a few granules. cu_count <= 0
+/* Split count from host-side values only, so that it holds under graph capture ("Native FP8 ...
+ * for Hopper", Design, Decode launches: static splits chosen from host-known sizes): the count
+ * fa8_decode_num_splits_for gives for the per-head decode kernel with one row block per
+ * (batch, kv head) (max_seqlen_q x heads_q / heads_kv <= 32): about 16 workgroups per compute
+ * unit over batch x heads_kv x splits, without splits shorter than four granules. cu_count <= 0
  * means 256 (MI355X). Always returns 1 .. FA8_MAX_SPLITS. */
 int32_t fa8_decode_num_splits(int32_t batch, int32_t heads_kv, int32_t max_seqlen_k, int32_t cu_count);
 
@@ -294,13 +326,21 @@ typedef struct {
   int64_t workgroups;
 } fa8_decode_plan_info;
 fa8_status fa8_decode_plan(const fa8_fwd_params* p, int32_t num_splits, fa8_decode_plan_info* info);
+/* The same for an explicit kernel choice (a fa8_decode_kernel value; FA8_ERR_UNSUPPORTED when that
+ * kernel cannot take the problem). */
+fa8_status fa8_decode_plan_ex(const fa8_fwd_params* p, int32_t num_splits, int32_t kernel,
+                              fa8_decode_plan_info* info);
 
 /* Bytes of o_partial + lse_partial for the given problem (o_partial first, then lse_partial,
- * each 256-byte aligned), or 0 on overflow. */
+ * each 256-byte aligned), or 0 on overflow: the caller-owned split-KV workspace, fp32 partial O
+ * and LSE per split ("Native FP8 ... for Hopper", Design, Decode launches: the split partials
+ * merged by the combine that the Performance section times inside each decode step). */
 size_t fa8_decode_workspace_bytes(int32_t num_splits, int32_t batch, int32_t max_seqlen_q,
                                   int32_t heads_q, int32_t dv);
 
-/* Thread-local description of the last non-OK status returned on this thread ("" if none). */
+/* Thread-local description of the last non-OK status returned on this thread ("" if none): the
+ * message behind FA8_ERR_INVALID / FA8_ERR_UNSUPPORTED, which the Hopper FP8 page's Design has
+ * raised for unsupported inputs (E5M2, mixed dtypes, MLA, block sparsity, other head dims). */
 const char* fa8_last_error(void);
 
 /* Library version string. */

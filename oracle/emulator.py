@@ -78,9 +78,21 @@ def e4m3_encode_rne(x: np.ndarray, saturate: bool = True) -> np.ndarray:
     return (code | sign).astype(np.uint8)
 
 
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """The value e4m3_encode_rne(x, saturate=True) encodes, computed directly for x >= 0 (the
+    emulator's P): with x = f 2^e, f in [0.5, 1), the E4M3 quantum is 2^(max(e, -5) - 4) (three
+    mantissa bits; subnormal spacing 2^-9 below 2^-6), the value is rounded to it with ties to
+    even, and 448 caps it. Returned as float64."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    _, e = np.frexp(x)
+    q = np.ldexp(1.0, np.maximum(e, -5) - 4)
+    return np.minimum(np.round(x / q) * q, E4M3_MAX)
+
+
 def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_splits: int = 1, sink_stage: str = "finalize",
             l_from_rounded: bool = False, heads: Optional[list] = None, batches: Optional[list] = None,
-            stats: Optional[dict] = None, interleave: int = 1, granule: Optional[int] = None):
+            stats: Optional[dict] = None, interleave: int = 1, granule: Optional[int] = None,
+            rows_of: Optional[dict] = None):
     """Run the method on every query row of the selected (batch, head) pairs.
 
     Splits cut the keys into contiguous runs of granules of `granule` keys (default tile_n;
@@ -91,7 +103,11 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
     KV range rescaled independently and merged by their LSEs, "Native FP8 (E4M3 Q/K/V) forward
     for Hopper", Design, Decode launches).
 
-    Returns a dict {(b, h): (O [Sq_b, dv] float64, LSE [Sq_b] float64)}.
+    rows_of, if given, maps a batch index to the query rows (indices into that sequence) to run;
+    every row's online softmax is independent of the others, so a subset gives exactly the rows
+    a full run gives.
+
+    Returns a dict {(b, h): (O [n, dv] float64, LSE [n] float64)}, n = Sq_b (or the subset).
     stats, if given, receives 'clipped' (number of P values that exceeded 448) and 'pmax'.
     """
     g_keys = granule if granule is not None else tile_n
@@ -115,7 +131,7 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
     out = {}
     clipped = 0
     pmax = 0.0
-    for b in (batches if batches is not None else range(B)):
+    for b in (batches if batches is not None else (sorted(rows_of) if rows_of is not None else range(B))):
         sq, sk = int(sq_all[b]), int(sk_all[b])
         # gather this batch's Q rows and K/V rows (by token index)
         if inp.cu_seqlens_q is not None:
@@ -134,21 +150,32 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
         else:
             kb, vb = inp.k[b, :sk], inp.v[b, :sk]
         i = np.arange(sq)
+        if rows_of is not None:
+            i = np.asarray(rows_of[b], np.int64)
+            qb = qb[i]
+        nr = len(i)
         ip = i + sk - sq
-        hi = np.full(sq, sk)
+        hi = np.full(nr, sk)
         wr = 0 if inp.causal else inp.window_right
         if wr >= 0:
             hi = np.minimum(hi, ip + wr + 1)
-        lo = np.zeros(sq, np.int64)
+        lo = np.zeros(nr, np.int64)
         if inp.window_left >= 0:
             lo = np.maximum(lo, ip - inp.window_left)
-        for h in (heads if heads is not None else range(Hq)):
-            kvh = h // g
+        # the query heads of one kv head share its K/V and its descales: their rows are stacked
+        # and run together (every row's online softmax is independent of the others)
+        sel_heads = list(heads if heads is not None else range(Hq))
+        for kvh in sorted(set(h // g for h in sel_heads)):
+            hs = [h for h in sel_heads if h // g == kvh]
+            nh = len(hs)
             c = np.float32(scale * desc(inp.q_descale, b, kvh) * desc(inp.k_descale, b, kvh) * LOG2E)
             dvs = desc(inp.v_descale, b, kvh)
-            qf = dec[qb[:, h, :]]                        # [sq, d] exact
+            qf = dec[np.concatenate([qb[:, h, :] for h in hs])]     # [nh * nr, d] exact
             kf = dec[kb[:, kvh, :]]                      # [sk, d]
             vf = dec[vb[:, kvh, :]]                      # [sk, dv]
+            lo_r, hi_r = np.tile(lo, nh), np.tile(hi, nh)
+            zrow = None if zs is None else np.repeat(np.asarray([zs[h] for h in hs], np.float64), nr)
+            n_all = nh * nr
             ntiles = (sk + tile_n - 1) // tile_n
             per = g_keys // tile_n
             ngran = (sk + g_keys - 1) // g_keys
@@ -156,15 +183,15 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
             for s, k in [(s, k) for s in range(num_splits) for k in range(interleave)]:
                 t0 = ((s * ngran) // num_splits) * per
                 t1 = min((((s + 1) * ngran) // num_splits) * per, ntiles)
-                m = np.full(sq, -np.inf, np.float32)
-                l = np.zeros(sq, np.float32)
-                o = np.zeros((sq, dv), np.float32)
+                m = np.full(n_all, -np.inf, np.float32)
+                l = np.zeros(n_all, np.float32)
+                o = np.zeros((n_all, dv), np.float32)
                 for t in range(t0, t1):
                     if t % interleave != k:
                         continue
                     js = np.arange(t * tile_n, min((t + 1) * tile_n, sk))
                     sc = (qf @ kf[js].T).astype(np.float32)          # exact dots, rounded to fp32
-                    vis = (js[None, :] >= lo[:, None]) & (js[None, :] < hi[:, None])
+                    vis = (js[None, :] >= lo_r[:, None]) & (js[None, :] < hi_r[:, None])
                     sc = np.where(vis, sc, np.float32(-np.inf))
                     mt = (sc.max(axis=1) * c).astype(np.float32)
                     with np.errstate(invalid="ignore"):
@@ -179,13 +206,13 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
                     if p.size:
                         pmax = max(pmax, float(p.max()))
                         clipped += int((p > E4M3_MAX).sum())
-                    p8 = dec[e4m3_encode_rne(p, saturate=True)]
+                    p8 = e4m3_round(p)
                     psum = p8.sum(axis=1) if l_from_rounded else p.astype(np.float64).sum(axis=1)
                     l = (alpha * l + psum.astype(np.float32)).astype(np.float32)
                     o_tile = (p8 @ vf[js]).astype(np.float32)
                     o = (alpha[:, None] * o + o_tile).astype(np.float32)
-                if zs is not None and sink_stage == "finalize":
-                    z2 = np.float32(zs[h] * LOG2E)
+                if zrow is not None and sink_stage == "finalize":
+                    z2 = (zrow * LOG2E).astype(np.float32)
                     mf = np.maximum(m, z2).astype(np.float32)
                     with np.errstate(invalid="ignore"):
                         a = np.where(np.isneginf(m), np.float32(0.0), np.exp2((m - mf).astype(np.float32))).astype(np.float32)
@@ -203,11 +230,13 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
                           for i in range(0, len(parts_o), interleave)]
                 parts_o = [x[0] for x in merged]
                 parts_l = [x[1] for x in merged]
-            zc = float(zs[h]) if (zs is not None and sink_stage == "combine") else None
+            zc = zrow if (zrow is not None and sink_stage == "combine") else None
             if num_splits == 1 and zc is None:
-                out[(b, h)] = (parts_o[0], parts_l[0])
+                ro, rl = parts_o[0], parts_l[0]
             else:
-                out[(b, h)] = combine(np.stack(parts_o), np.stack(parts_l), sink=zc)
+                ro, rl = combine(np.stack(parts_o), np.stack(parts_l), sink=zc)
+            for j, h in enumerate(hs):
+                out[(b, h)] = (ro[j * nr:(j + 1) * nr], rl[j * nr:(j + 1) * nr])
     if stats is not None:
         stats["clipped"] = clipped
         stats["pmax"] = pmax

@@ -51,12 +51,56 @@ def dequantize(inp):
     return q, k, v
 
 
-def emulate_mx(inp, tile_n: int = 128, tau: float = 0.75, rule: str = "ceil", stats=None):
-    assert rule in ("ceil", "floor")
+def _run_rows(q, k, v, b, h, kvh, i, Sq, Sk, c, tau, rule, lo_all, hi_all, dec, dv, counter):
+    """The method on query rows i (indices into the sequence) of (batch b, query head h)."""
+    lo, hi = lo_all[i], hi_all[i]
+    nr = len(i)
+    m = np.full(nr, -np.inf, np.float32)
+    l = np.zeros(nr, np.float32)
+    o = np.zeros((nr, dv), np.float32)
+    qr = q[b, i, h]
+    for t0 in range(0, Sk, counter["tile_n"]):
+        js = np.arange(t0, min(t0 + counter["tile_n"], Sk))
+        sc = (qr @ k[b, js, kvh].T).astype(np.float32)
+        vis = (js[None, :] >= lo[:, None]) & (js[None, :] < hi[:, None])
+        sc = np.where(vis, sc, np.float32(-np.inf))
+        mt = (sc.max(axis=1) * c).astype(np.float32)
+        with np.errstate(invalid="ignore"):
+            move = (mt - m) > np.float32(tau)
+        with np.errstate(over="ignore", invalid="ignore"):
+            alpha = np.where(move, np.exp2((m - np.where(move, mt, 0)).astype(np.float32)), np.float32(1.0))
+        alpha = np.where(move & np.isneginf(m), np.float32(0.0), alpha).astype(np.float32)
+        m = np.where(move, mt, m).astype(np.float32)
+        x = (sc.astype(np.float64) * np.float64(c)).astype(np.float32)      # log2 units
+        p8s = np.zeros_like(x, dtype=np.float64)                           # stored P times scale
+        live = ~np.isneginf(m)
+        msafe = np.where(live, m, np.float32(0.0))
+        for j0 in range(0, len(js), 32):
+            blk = slice(j0, j0 + 32)
+            with np.errstate(invalid="ignore"):
+                y = (x[:, blk].max(axis=1) - msafe).astype(np.float32)
+            if rule == "ceil":
+                X = np.ceil(y.astype(np.float64) - LOG2_448)
+            else:
+                X = np.floor(y.astype(np.float64)) - 8.0
+            X = np.where(np.isfinite(X) & live, np.clip(X, -127, 127), -127.0)
+            arg = (x[:, blk].astype(np.float64) - msafe[:, None] - X[:, None]).astype(np.float32)
+            p = np.where(live[:, None], np.exp2(arg), np.float32(0.0)).astype(np.float32)
+            counter["clipped"] += int((p > 448.0).sum())
+            p8s[:, blk] = dec[e4m3_encode_rne(p, saturate=True)] * np.exp2(X)[:, None]
+        p8s = np.where(vis, p8s, 0.0)
+        l = (alpha * l + p8s.sum(axis=1).astype(np.float32)).astype(np.float32)
+        o_tile = (p8s @ v[b, js, kvh]).astype(np.float32)
+        o = (alpha[:, None] * o + o_tile).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        on = np.where(l[:, None] > 0, o.astype(np.float64) / l[:, None], 0.0)
+        ln = np.where(l > 0, math.log(2.0) * (m.astype(np.float64) + np.log2(np.where(l > 0, l, 1.0))), -np.inf)
+    return on, ln
+
+
+def _setup(inp):
     q, k, v = dequantize(inp)
-    dec = e4m3_table()
-    B, Sq, Sk, Hq, Hkv, dv = inp.batch, inp.max_seqlen_q, inp.max_seqlen_k, inp.heads_q, inp.heads_kv, inp.dv
-    g = Hq // Hkv
+    Sq, Sk = inp.max_seqlen_q, inp.max_seqlen_k
     scale = inp.softmax_scale if inp.softmax_scale and inp.softmax_scale > 0 else 1.0 / math.sqrt(inp.d)
     c = np.float32(scale * LOG2E)
     i = np.arange(Sq)
@@ -68,49 +112,41 @@ def emulate_mx(inp, tile_n: int = 128, tau: float = 0.75, rule: str = "ceil", st
     lo = np.zeros(Sq, np.int64)
     if inp.window_left >= 0:
         lo = np.maximum(lo, ip - inp.window_left)
+    return q, k, v, c, lo, hi
+
+
+def emulate_mx(inp, tile_n: int = 128, tau: float = 0.75, rule: str = "ceil", stats=None):
+    """Every row: O [B, Sq, Hq, dv] and LSE [B, Hq, Sq] (float64)."""
+    assert rule in ("ceil", "floor")
+    q, k, v, c, lo, hi = _setup(inp)
+    dec = e4m3_table()
+    B, Sq, Sk, Hq, Hkv, dv = inp.batch, inp.max_seqlen_q, inp.max_seqlen_k, inp.heads_q, inp.heads_kv, inp.dv
+    g = Hq // Hkv
     out = np.zeros((B, Sq, Hq, dv))
     lse = np.full((B, Hq, Sq), -np.inf)
-    clipped = 0
+    counter = {"clipped": 0, "tile_n": tile_n}
+    rows = np.arange(Sq)
     for b in range(B):
         for h in range(Hq):
-            kvh = h // g
-            m = np.full(Sq, -np.inf, np.float32)
-            l = np.zeros(Sq, np.float32)
-            o = np.zeros((Sq, dv), np.float32)
-            for t0 in range(0, Sk, tile_n):
-                js = np.arange(t0, min(t0 + tile_n, Sk))
-                sc = (q[b, :, h] @ k[b, js, kvh].T).astype(np.float32)
-                vis = (js[None, :] >= lo[:, None]) & (js[None, :] < hi[:, None])
-                sc = np.where(vis, sc, np.float32(-np.inf))
-                mt = (sc.max(axis=1) * c).astype(np.float32)
-                with np.errstate(invalid="ignore"):
-                    move = (mt - m) > np.float32(tau)
-                alpha = np.where(move, np.exp2((m - np.where(move, mt, 0)).astype(np.float32)), np.float32(1.0))
-                alpha = np.where(move & np.isneginf(m), np.float32(0.0), alpha).astype(np.float32)
-                m = np.where(move, mt, m).astype(np.float32)
-                x = (sc.astype(np.float64) * np.float64(c)).astype(np.float32)      # log2 units
-                p8s = np.zeros_like(x, dtype=np.float64)                           # stored P times scale
-                for j0 in range(0, len(js), 32):
-                    blk = slice(j0, j0 + 32)
-                    with np.errstate(invalid="ignore"):
-                        y = (x[:, blk].max(axis=1) - m).astype(np.float32)
-                    if rule == "ceil":
-                        X = np.ceil(y.astype(np.float64) - LOG2_448)
-                    else:
-                        X = np.floor(y.astype(np.float64)) - 8.0
-                    X = np.where(np.isfinite(X), np.clip(X, -127, 127), -127.0)
-                    arg = (x[:, blk].astype(np.float64) - m[:, None] - X[:, None]).astype(np.float32)
-                    p = np.where(np.isneginf(m)[:, None], np.float32(0.0), np.exp2(arg)).astype(np.float32)
-                    clipped += int((p > 448.0).sum())
-                    p8s[:, blk] = dec[e4m3_encode_rne(p, saturate=True)] * np.exp2(X)[:, None]
-                p8s = np.where(vis, p8s, 0.0)
-                l = (alpha * l + p8s.sum(axis=1).astype(np.float32)).astype(np.float32)
-                o_tile = (p8s @ v[b, js, kvh]).astype(np.float32)
-                o = (alpha[:, None] * o + o_tile).astype(np.float32)
-            with np.errstate(divide="ignore", invalid="ignore"):
-                out[b, :, h] = np.where(l[:, None] > 0, o.astype(np.float64) / l[:, None], 0.0)
-                lse[b, h] = np.where(l > 0, math.log(2.0) * (m.astype(np.float64) +
-                                                             np.log2(np.where(l > 0, l, 1.0))), -np.inf)
+            out[b, :, h], lse[b, h] = _run_rows(q, k, v, b, h, h // g, rows, Sq, Sk, c, tau, rule, lo, hi, dec, dv,
+                                               counter)
     if stats is not None:
-        stats["clipped"] = clipped
+        stats["clipped"] = counter["clipped"]
     return out, lse
+
+
+def emulate_mx_rows(inp, rows_of: dict, heads=None, tile_n: int = 128, tau: float = 0.75, rule: str = "ceil"):
+    """The rows rows_of[b] (indices into sequence b) of the query heads `heads` (default all):
+    {(b, h): (O [n, dv], LSE [n])}. Rows are independent in the method, so these equal the rows
+    of a full run."""
+    q, k, v, c, lo, hi = _setup(inp)
+    dec = e4m3_table()
+    g = inp.heads_q // inp.heads_kv
+    counter = {"clipped": 0, "tile_n": tile_n}
+    res = {}
+    for b in sorted(rows_of):
+        i = np.asarray(rows_of[b], np.int64)
+        for h in (heads if heads is not None else range(inp.heads_q)):
+            res[(b, h)] = _run_rows(q, k, v, b, h, h // g, i, inp.max_seqlen_q, inp.max_seqlen_k, c, tau, rule, lo,
+                                    hi, dec, inp.dv, counter)
+    return res

@@ -1,8 +1,34 @@
-"""Shared test helpers: move seeded inputs to the GPU, call the C ABI through the binding,
-compare with the CPU oracle. Test infrastructure only."""
+"""Shared test helpers: move seeded inputs to the GPU, call the C ABI through the binding, and
+judge a kernel result against the CPU oracle. Test infrastructure only.
+
+One parity rule for every GPU test (``check_rows``; ``check_against_oracle`` applies it to every
+row of a small problem):
+
+1. no NaN, and the LSE is -inf on exactly the rows the oracle gives -inf (no visible key);
+2. elements beyond the stated tolerance, |got - ref| > 2e-2 + 2e-2 |ref| on the fp16/bf16
+   output, are counted and printed, and their count is capped at one in a thousand elements;
+3. every element lies inside the method's own error bound (``method_bound_rows``): a bound
+   derived from the arithmetic of the method, independent of any tile or split schedule;
+4. the elements beyond 2e-2 must be the method's own misses: the method emulator at its pinned
+   default schedule (64-key tiles, one running state; the split partition the ABI documents for
+   split-KV results) must miss at least four in five of them (all but one when there are fewer
+   than ten) by half the tolerance or more (its rounding pattern depends on where the running
+   max settles, so the same few borderline elements cannot be expected to agree one for one);
+5. the LSE lies within the method's LSE bound on every row, and within 1e-2 on every row that
+   sees at least 256 keys;
+6. bug detector: when the emulator can run the schedule the ABI documents for the entry point
+   (fa8.h: the prefill's KV tile, fa8_decode_plan for the decode), RMS(kernel - that emulator)
+   must stay below 0.35 RMS(emulator - oracle) + 1e-4. This can only fail a test.
+
+Each check prints one line; when the environment variable FA8_PARITY_RECORD names a file, a JSON
+line per check is appended to it.
+"""
 from __future__ import annotations
 
+import copy
+import json
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -14,8 +40,19 @@ from fa8_fwd_amd import binding
 ATOL = 2e-2
 RTOL = 2e-2
 LSE_ATOL = 1e-2
+CAP = 1e-3                 # at most one element in a thousand beyond ATOL + RTOL |ref|
+LSE_MANY_KEYS = 256        # rows with at least this many visible keys must meet LSE_ATOL
 GRANULE = binding.SPLIT_GRANULE
 BLOCK_ROWS = binding.DECODE_BLOCK_ROWS
+# The FP8 MFMA computes each dot product of E4M3 (optionally block-scaled) operands with an error
+# below MFMA_DOT_REL times the sum of the absolute products (measured on gfx950 by
+# tests/test_mfma_precision_gpu.py: at most 2^-14.3 over random-scale and plain E4M3 data); every
+# score the kernels compute carries this, the exact oracle does not.
+MFMA_DOT_REL = 2.0 ** -13
+P_ROUND = 2.0 ** -4        # relative rounding of an E4M3 value (3 mantissa bits, nearest even)
+# Largest LSE error of the method without the score term: l is a sum of E4M3-rounded P, so
+# |sum p~ / sum p - 1| <= 2^-4.
+LSE_METHOD = -math.log(1 - P_ROUND) + 1e-4
 
 
 def dev():
@@ -52,30 +89,39 @@ def sink_tensor(inp):
     return None if z is None else to_dev(np.asarray(z, np.float32))
 
 
-def run_prefill(inp, return_lse=True):
+def run_prefill(inp):
     q, k, v, kw = tensors(inp)
     out, lse = binding.prefill(q, k, v, out_dtype=out_dtype(inp), return_lse=True, sink=sink_tensor(inp), **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def decode_schedule(inp, num_splits):
-    """(block_keys, key_groups) of the decode kernel the library picks (fa8_decode_plan)."""
+def decode_splits(inp, num_splits=None):
+    """The split count a decode call uses (the library's heuristic when num_splits is None)."""
+    if num_splits is not None:
+        return int(num_splits)
     q, k, v, kw = tensors(inp)
-    plan = binding.decode_plan(q, k, v, num_splits=num_splits, **kw)
+    return binding.decode_num_splits_for(q, k, v, **kw)
+
+
+def decode_schedule(inp, num_splits, kernel=-1):
+    """(block_keys, key_groups) of the decode kernel a launch uses (fa8_decode_plan)."""
+    q, k, v, kw = tensors(inp)
+    plan = binding.decode_plan(q, k, v, num_splits=num_splits, kernel=kernel, **kw)
     return plan["block_keys"], plan["key_groups"]
 
 
-def run_decode(inp, num_splits=None):
+def run_decode(inp, num_splits=None, kernel=-1):
     q, k, v, kw = tensors(inp)
-    out, lse = binding.decode(q, k, v, num_splits=num_splits, out_dtype=out_dtype(inp), return_lse=True,
-                              sink=sink_tensor(inp), **kw)
+    out, lse = binding.decode(q, k, v, num_splits=num_splits, kernel=kernel, out_dtype=out_dtype(inp),
+                              return_lse=True, sink=sink_tensor(inp), **kw)
     torch.cuda.synchronize()
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
 def compare(got: np.ndarray, ref: np.ndarray, what: str = "", atol=ATOL, rtol=RTOL):
-    """allclose at the benchmark spec's tolerance; returns (max abs err, rel-RMS err)."""
+    """Every element within atol + rtol |ref| (no exceptions); returns (max abs err, rel-RMS err).
+    For results with no method rounding in them (the combine of given partials)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -100,13 +146,6 @@ def compare_lse(got, ref, what=""):
     if (~inf_r).any():
         e = np.abs(got[~inf_r] - ref[~inf_r]).max()
         assert e <= LSE_ATOL, f"{what}: LSE max abs err {e}"
-
-
-def rows_layout(inp, o_rows):
-    """Reshape oracle rows (all_rows order) to the output layout."""
-    if inp.cu_seqlens_q is not None:
-        return o_rows.reshape(int(inp.cu_seqlens_q[-1]), inp.heads_q, -1)
-    return o_rows.reshape(inp.batch, inp.max_seqlen_q, inp.heads_q, -1)
 
 
 def split_key_ranges(inp, num_splits: int):
@@ -148,141 +187,263 @@ def split_key_ranges(inp, num_splits: int):
 
 
 def prefill_tile(d: int, dv: int) -> int:
-    """KV tile of the prefill kernel: 128 keys when d + dv <= 256, else 64 (the lazy-rescale
-    decisions, and so the exact rounding, depend on the tile the kernel uses)."""
+    """KV tile of fa8_fwd_prefill as include/fa8.h states it: 128 keys when d + dv <= 256, else
+    64 (one online-softmax step per tile)."""
     return 128 if d + dv <= 256 else 64
 
 
-def emulate_full(inp, num_splits: int = 1, with_lse: bool = False, tile_n: int = GRANULE, **kw):
-    # kw: passed to the emulator (interleave, granule, l_from_rounded, ...)
-    """The oracle package's step-by-step method emulator, reshaped to the output layout (and the
-    LSE to [B, Hq, Sq] / [Hq, total_q] when with_lse)."""
-    from oracle import emulator
-    kw.setdefault("l_from_rounded", True)      # the kernel sums the rounded P
-    res = emulator.emulate(inp, tile_n=tile_n, num_splits=num_splits, **kw)
+# ---------------------------------------------------------------------------------------------
+# Per-row quantities of the rule
+# ---------------------------------------------------------------------------------------------
+
+def gather(inp, o_full, l_full, rows):
+    """Kernel output and LSE at the oracle's rows (output layout [B,Sq,Hq,dv] / [total_q,Hq,dv],
+    LSE [B,Hq,Sq] / [Hq,total_q])."""
+    rb, rh, ri = (np.asarray(x, np.int64) for x in rows)
     if inp.cu_seqlens_q is not None:
-        tot = int(inp.cu_seqlens_q[-1])
-        out = np.zeros((tot, inp.heads_q, inp.dv))
-        lse = np.full((inp.heads_q, tot), -np.inf)
-        for (b, h), (o, l) in res.items():
-            a, z = inp.cu_seqlens_q[b], inp.cu_seqlens_q[b + 1]
-            out[a:z, h] = o
-            lse[h, a:z] = l
-    else:
-        out = np.zeros((inp.batch, inp.max_seqlen_q, inp.heads_q, inp.dv))
-        lse = np.full((inp.batch, inp.heads_q, inp.max_seqlen_q), -np.inf)
-        for (b, h), (o, l) in res.items():
-            out[b, :, h] = o
-            lse[b, h] = l
-    # the method's last step: round to the output dtype (RNE), as the kernel's store does
-    out = torch.from_numpy(out).to(out_dtype(inp)).double().numpy()
-    return (out, lse) if with_lse else out
+        t = np.asarray(inp.cu_seqlens_q, np.int64)[rb] + ri
+        return o_full[t, rh], l_full[rh, t]
+    return o_full[rb, ri, rh], l_full[rb, rh, ri]
 
 
-def method_bound(inp, ref: np.ndarray) -> np.ndarray:
-    """Per-element error bound of the method from its arithmetic. Each P element is rounded to
-    E4M3: p~ = p (1 + e), |e| <= 2^-4 in the normal range; subnormals (P < 2^-6, while the row's
-    largest P is >= 2^8) carry an absolute error <= 2^-10, i.e. < 2^-18 of the row sum each.
-    With the row sum taken over the rounded P, O = sum w_j (1 + e_j) v_j / sum w_j (1 + e_j), so
-    |O - O_ref| <= 2^-4/(1 - 2^-4) * (sum_j w_j |v_j| + |O_ref|) + Sk 2^-17 max|v|, plus the
-    output rounding (bf16: 2^-8 relative, fp16: 2^-11) and ~1e-4 for fp32 accumulation.
-    sum_j w_j |v_j| (with the v descale) comes from the oracle run on |V| (sign bits cleared)."""
-    import copy
+def row_bounds(inp, rows):
+    """[lo, hi) visible key range of each row: bottom-right causal alignment and window bounds."""
+    rb, _, ri = (np.asarray(x, np.int64) for x in rows)
+    sq, sk = (np.asarray(x, np.int64) for x in oracle.seqlens(inp))
+    ip = ri + sk[rb] - sq[rb]
+    wr = 0 if inp.causal else inp.window_right
+    hi = np.minimum(sk[rb], ip + wr + 1) if wr >= 0 else sk[rb]
+    lo = np.maximum(0, ip - inp.window_left) if inp.window_left >= 0 else np.zeros_like(ip)
+    return lo, np.maximum(hi, lo)
+
+
+def visible_keys(inp, rows):
+    lo, hi = row_bounds(inp, rows)
+    return hi - lo
+
+
+def _descale_at(x, b, kvh):
+    if x is None:
+        return np.ones(len(b))
+    a = np.asarray(x, np.float64)
+    if a.ndim == 0:
+        return np.full(len(b), float(a))
+    return a[np.where(a.shape[0] > 1, b, 0), np.where(a.shape[1] > 1, kvh, 0)]
+
+
+def _dequant_rows(inp):
+    """Callables giving dequantized fp64 Q rows and K rows (E4M3 values times MX block scales when
+    the input carries them; descales not applied)."""
+    t = oracle.e4m3_table()
+    e8 = lambda e: np.ldexp(1.0, np.asarray(e, np.int64) - 127)
+    sq_all, sk_all = oracle.seqlens(inp)
+    qmx, kmx = getattr(inp, "q_mx", None), getattr(inp, "k_mx", None)
+
+    def q_row(b, i, h):
+        if inp.cu_seqlens_q is not None:
+            x = t[inp.q[int(inp.cu_seqlens_q[b]) + i, h]]
+        else:
+            x = t[inp.q[b, i, h]]
+        if qmx is not None:
+            x = (x.reshape(-1, 32) * e8(qmx[b, i, h])[:, None]).reshape(-1)
+        return x
+
+    def k_rows(b, kvh):
+        sk = int(sk_all[b])
+        j = np.arange(sk)
+        if inp.block_table is not None:
+            kk = inp.k[inp.block_table[b, j // inp.page_size], j % inp.page_size, kvh]
+        elif inp.cu_seqlens_k is not None:
+            k0 = int(inp.cu_seqlens_k[b])
+            kk = inp.k[k0:k0 + sk, kvh]
+        else:
+            kk = inp.k[b, :sk, kvh]
+        x = t[kk]
+        if kmx is not None:
+            x = (x.reshape(sk, -1, 32) * e8(kmx[b, :sk, kvh])[:, :, None]).reshape(sk, -1)
+        return x
+
+    return q_row, k_rows
+
+
+def score_error(inp, rows):
+    """Per row, the largest error the FP8 MFMA can put into one of its scaled scores, in natural-log
+    units: MFMA_DOT_REL * softmax_scale * dq * dk * max over visible keys of sum_i |q_i k_ji|."""
+    rb, rh, ri = (np.asarray(x, np.int64) for x in rows)
+    g = inp.heads_q // inp.heads_kv
+    scale = inp.softmax_scale if inp.softmax_scale and inp.softmax_scale > 0 else 1.0 / math.sqrt(inp.d)
+    lo, hi = row_bounds(inp, rows)
+    q_row, k_rows = _dequant_rows(inp)
+    out = np.zeros(len(rb))
+    kvh = rh // g
+    for b, kh in sorted(set(zip(rb.tolist(), kvh.tolist()))):
+        sel = np.nonzero((rb == b) & (kvh == kh) & (hi > lo))[0]
+        if not len(sel):
+            continue
+        ka = np.abs(k_rows(b, kh))                                        # [sk, d]
+        qa = np.abs(np.stack([q_row(b, int(ri[n]), int(rh[n])) for n in sel]))   # [n, d]
+        prod = qa @ ka.T                                                  # [n, sk]
+        j = np.arange(ka.shape[0])[None, :]
+        vis = (j >= lo[sel, None]) & (j < hi[sel, None])
+        out[sel] = np.where(vis, prod, 0.0).max(axis=1)
+    ds = _descale_at(inp.q_descale, rb, kvh) * _descale_at(inp.k_descale, rb, kvh)
+    return MFMA_DOT_REL * scale * ds * out
+
+
+def method_bound_rows(inp, rows, ref, delta):
+    """Per-element error bound of the method at these rows. Each P the kernel multiplies is the
+    exact weight w_j times r_j = (1 + e_j) exp(eta_j): the E4M3 rounding |e_j| <= 2^-4 (normal
+    range; a subnormal P < 2^-6 while the row's largest P is >= 2^7.25 carries an absolute error
+    <= 2^-10, below 2^-17 of the row sum) and the score error |eta_j| <= delta of the row. With
+    the row sum taken over the same P, O - O_ref = sum_j w_j (r_j - 1)(v_j - O_ref) / sum_j w_j r_j,
+    so with rho = (1 + 2^-4) e^delta - 1:
+      |O - O_ref| <= rho / (1 - rho) * (sum_j w_j |v_j| + |O_ref|) + Sk 2^-17 max|v|
+    plus the output rounding (bf16 2^-8, fp16 2^-11 relative) and 1e-4 for fp32 accumulation.
+    sum_j w_j |v_j| (with the v descale) is the oracle run on |V| (sign bits cleared)."""
     absinp = copy.copy(inp)
     absinp.v = inp.v & np.uint8(0x7F)
-    a, _ = oracle.attention_full(absinp)
+    a, _ = oracle.attention(absinp, rows=rows)
     _, sk = oracle.seqlens(inp)
-    table = oracle.e4m3_table()
-    vmax = float(np.nanmax(np.abs(table[inp.v])))
+    vmax = float(np.nanmax(np.abs(oracle.e4m3_table()[inp.v])))
     if getattr(inp, "v_mx", None) is not None:       # MXFP8 V: the largest block scale
         vmax *= 2.0 ** (int(np.max(inp.v_mx)) - 127)
     dvmax = float(np.max(inp.v_descale)) if inp.v_descale is not None else 1.0
     out_rel = 2.0 ** -11 if inp.out_dtype == "fp16" else 2.0 ** -8
-    e = 2.0 ** -4 / (1 - 2.0 ** -4)
-    return e * (a + np.abs(ref)) + float(sk.max()) * 2.0 ** -17 * vmax * dvmax + out_rel * np.abs(ref) + 1e-4
+    rho = (1 + P_ROUND) * np.exp(np.asarray(delta, np.float64)) - 1
+    with np.errstate(divide="ignore"):
+        e = np.where(rho < 1, rho / (1 - rho), np.inf)[:, None]
+    b = e * (a + np.abs(ref)) + float(sk.max()) * 2.0 ** -17 * vmax * dvmax + out_rel * np.abs(ref) + 1e-4
+    # O and O_ref are both weighted means of the same V rows: never further apart than 2 max|v|
+    return np.minimum(b, 2 * vmax * dvmax * (1 + out_rel) + 1e-4)
 
 
-def compare_bound(got, ref, bound, what=""):
-    got = np.asarray(got, np.float64)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = np.abs(got - ref)
-    bad = err > bound
-    if bad.any():
-        idx = np.argwhere(bad)[:5]
-        raise AssertionError(f"{what}: {int(bad.sum())} elements beyond the method's rounding bound; first at "
-                             f"{idx.tolist()} err {[float(err[tuple(i)]) for i in idx]} "
-                             f"bound {[float(bound[tuple(i)]) for i in idx]}")
+# ---------------------------------------------------------------------------------------------
+# Emulator runs at given rows
+# ---------------------------------------------------------------------------------------------
+
+def emulate_rows(inp, rows, **kw):
+    """The method emulator (oracle.emulator) at the given rows: O rounded to the output dtype (RNE,
+    as the kernel's store) and LSE. kw: its schedule options (tile_n, num_splits, sink_stage,
+    interleave, granule); the row sum is over the rounded P (reading 8 of the design)."""
+    from oracle import emulator
+    rb, rh, ri = (np.asarray(x, np.int64) for x in rows)
+    kw.setdefault("l_from_rounded", True)
+    rows_of = {int(b): np.unique(ri[rb == b]) for b in np.unique(rb)}
+    res = emulator.emulate(inp, rows_of=rows_of, heads=sorted(set(rh.tolist())), **kw)
+    o = np.zeros((len(rb), inp.dv))
+    l = np.full(len(rb), -np.inf)
+    for n in range(len(rb)):
+        b, h = int(rb[n]), int(rh[n])
+        k = int(np.searchsorted(rows_of[b], ri[n]))
+        eo, el = res[(b, h)]
+        o[n] = eo[k]
+        l[n] = el[k]
+    o = torch.from_numpy(o).to(out_dtype(inp)).double().numpy()
+    return o, l
 
 
-def compare_to_emulator(got, emu, ref, what=""):
-    """The kernel follows the method step by step, so it must sit much closer to the emulator
-    than either sits to the exact reference (rare one-ulp E4M3 flips of P are the only source of
-    difference). Requires RMS(kernel - emu) <= 0.35 * RMS(emu - ref) + 1e-4."""
-    got = np.asarray(got, np.float64)
-    d_ke = math.sqrt(float(np.mean((got - emu) ** 2)))
-    d_er = math.sqrt(float(np.mean((emu - ref) ** 2)))
-    assert d_ke <= 0.35 * d_er + 1e-4, f"{what}: kernel-emulator RMS {d_ke:.3g} vs emulator-oracle RMS {d_er:.3g}"
-    return d_ke, d_er
+def emulate_mx_rows(inp, rows, **kw):
+    """The MXFP8 method emulator (oracle.emulator_mx) at the given rows, O rounded to the output
+    dtype."""
+    from oracle import emulator_mx
+    rb, rh, ri = (np.asarray(x, np.int64) for x in rows)
+    rows_of = {int(b): np.unique(ri[rb == b]) for b in np.unique(rb)}
+    res = emulator_mx.emulate_mx_rows(inp, rows_of, heads=sorted(set(rh.tolist())), **kw)
+    o = np.zeros((len(rb), inp.dv))
+    l = np.full(len(rb), -np.inf)
+    for n in range(len(rb)):
+        b, h = int(rb[n]), int(rh[n])
+        k = int(np.searchsorted(rows_of[b], ri[n]))
+        eo, el = res[(b, h)]
+        o[n] = eo[k]
+        l[n] = el[k]
+    o = torch.from_numpy(o).to(out_dtype(inp)).double().numpy()
+    return o, l
 
 
-# Largest LSE error of the method: l is a sum of E4M3-rounded P, |sum p~ / sum p - 1| <= 2^-4.
-LSE_METHOD = -math.log(1 - 2.0 ** -4) + 1e-4
+# ---------------------------------------------------------------------------------------------
+# The rule
+# ---------------------------------------------------------------------------------------------
+
+def _record(entry: dict):
+    path = os.environ.get("FA8_PARITY_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(entry) + "\n")
 
 
-def check_against_oracle(inp, got, glse, what, strict=True, emu=True, num_splits=1, tile_n=GRANULE,
-                         interleave=1, granule=None, sink_stage="finalize"):
-    """Parity of one kernel result with the oracle.
-
-    strict: every element within 2e-2 + 2e-2 |ref| (the stated tolerance), except elements where
-      the method itself (the emulator) misses it by the same amount: those must stay inside the
-      method's rounding bound with |kernel - emulator| <= |emulator - ref| / 4 + 2^-8 |ref| + 2e-3.
-      Needs emu; their count is reported.
-    not strict: every element inside the method's rounding bound (few-key rows, sharp softmax).
-    LSE: within the method's bound -ln(1 - 2^-4); rows beyond 1e-2 are counted and reported.
-    emu: also the global kernel-emulator RMS check of compare_to_emulator; the emulator runs the
-      kernel's schedule (tile_n keys per step, `interleave` running states per split, splits cut
-      on `granule`-key granules).
-    Returns a one-line summary."""
-    ref, rlse = oracle.attention_full(inp)
-    got = np.asarray(got, np.float64)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    err = np.abs(got - ref)
-    bound = method_bound(inp, ref)
-    emu_o = emu_l = None
-    if emu:
-        emu_o, emu_l = emulate_full(inp, num_splits=num_splits, with_lse=True, tile_n=tile_n, interleave=interleave,
-                                    granule=granule, sink_stage=sink_stage)
-    n_method = 0
-    if strict:
-        bad = err > ATOL + RTOL * np.abs(ref)
-        if bad.any():
-            if emu_o is None:
-                compare(got, ref, what)        # raises with details
-            same = np.abs(got - emu_o) <= 0.25 * np.abs(emu_o - ref) + 2.0 ** -8 * np.abs(ref) + 2e-3
-            ok = same & (err <= bound)
-            if not ok[bad].all():
-                idx = np.argwhere(bad & ~ok)[:5]
-                raise AssertionError(
-                    f"{what}: {int((bad & ~ok).sum())} elements outside 2e-2 abs/rel not explained by the method: "
-                    f"at {idx.tolist()} got {[float(got[tuple(i)]) for i in idx]} ref {[float(ref[tuple(i)]) for i in idx]} "
-                    f"emulator {[float(emu_o[tuple(i)]) for i in idx]}")
-            n_method = int(bad.sum())
+def check_rows(inp, rows, o, l, what, emu_default=None, emu_sched=None, ref=None):
+    """The parity rule (module docstring) on the given rows. o: [n, dv] kernel output, l: [n] its
+    LSE; emu_default / emu_sched: (O, LSE) of the emulator at the default / the documented
+    schedule, or None. Returns a one-line summary."""
+    if ref is None:
+        ref, rlse = oracle.attention(inp, rows=rows)
     else:
-        compare_bound(got, ref, bound, what)
-    # LSE
-    glse = np.asarray(glse, np.float64)
-    inf_r = np.isneginf(rlse)
-    assert np.array_equal(np.isneginf(glse), inf_r), f"{what}: -inf pattern of LSE differs"
-    le = np.abs(np.where(inf_r, 0.0, glse - rlse))
-    # the LSE of a row with few keys carries the relative rounding of its sum of E4M3 P values
-    assert le.max(initial=0.0) <= LSE_METHOD, f"{what}: LSE max abs err {le.max():.3g} beyond the method bound"
-    n_lse = int((le > LSE_ATOL).sum())
+        ref, rlse = ref
+    o = np.asarray(o, np.float64)
+    l = np.asarray(l, np.float64)
+    assert o.shape == ref.shape, (o.shape, ref.shape)
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    assert np.array_equal(np.isneginf(l), np.isneginf(rlse)), f"{what}: -inf pattern of LSE differs"
+    assert not np.isnan(l).any(), f"{what}: NaN in LSE"
+    n_el = o.size
+    err = np.abs(o - ref)
+    tol = ATOL + RTOL * np.abs(ref)
+    bad = err > tol
+    n_bad = int(bad.sum())
+    cap = int(CAP * n_el)
+    delta = score_error(inp, rows)
+    bound = method_bound_rows(inp, rows, ref, delta)
+    over = err > bound
+    assert not over.any(), (f"{what}: {int(over.sum())} elements beyond the method's error bound, first at "
+                            f"{np.argwhere(over)[:3].tolist()} err {err[over][:3].tolist()} bound {bound[over][:3].tolist()}")
+    assert n_bad <= cap, f"{what}: {n_bad}/{n_el} elements beyond 2e-2 abs/rel, cap {cap}"
+    n_unexpl = 0
+    if n_bad and emu_default is not None:
+        missed = np.abs(np.asarray(emu_default[0], np.float64) - ref) > 0.5 * tol
+        n_unexpl = int((bad & ~missed).sum())
+        assert n_unexpl <= max(1, n_bad // 5), (f"{what}: {n_unexpl} of the {n_bad} elements beyond 2e-2 are not "
+                                                f"missed by the method at its default schedule")
+    fin = np.isfinite(rlse)
+    le = np.abs(np.where(fin, l - np.where(fin, rlse, 0.0), 0.0))
+    lbound = LSE_METHOD + delta
+    assert np.all(le <= lbound), f"{what}: LSE err {le.max():.3g} beyond the method's LSE bound"
+    many = visible_keys(inp, rows) >= LSE_MANY_KEYS
+    lse_many = float(le[many].max(initial=0.0))
+    assert lse_many <= LSE_ATOL, f"{what}: LSE err {lse_many:.3g} > 1e-2 on a row with >= {LSE_MANY_KEYS} keys"
     rms = math.sqrt(float(np.mean(ref ** 2))) if ref.size else 0.0
-    rel = math.sqrt(float(np.mean((got - ref) ** 2))) / rms if rms > 0 else 0.0
-    msg = (f"{what}: max abs err {err.max():.3e} rel-RMS {rel * 100:.3f}% beyond-2e-2-as-method "
-           f"{n_method}/{err.size} lse-max {le.max(initial=0.0):.2e} lse>1e-2 {n_lse}/{le.size}")
-    if emu:
-        d_ke, d_er = compare_to_emulator(got, emu_o, ref, what)
+    rel = math.sqrt(float(np.mean((o - ref) ** 2))) / rms if rms > 0 else 0.0
+    entry = dict(what=what, elements=n_el, beyond_2e2=n_bad, cap=cap, not_missed_by_default_emulator=n_unexpl,
+                 max_abs_err=float(err.max(initial=0.0)), rel_rms=rel, lse_max_err=float(le.max(initial=0.0)),
+                 lse_max_err_rows_256_keys=lse_many)
+    msg = (f"{what}: max abs err {entry['max_abs_err']:.3e} rel-RMS {rel * 100:.3f}% beyond-2e-2 {n_bad}/{n_el} "
+           f"(cap {cap}, not missed by the default emulator {n_unexpl}) LSE max err {entry['lse_max_err']:.2e} "
+           f"(rows >= {LSE_MANY_KEYS} keys {lse_many:.2e})")
+    if emu_sched is not None:
+        es = np.asarray(emu_sched[0], np.float64)
+        d_ke = math.sqrt(float(np.mean((o - es) ** 2)))
+        d_er = math.sqrt(float(np.mean((es - ref) ** 2)))
+        assert d_ke <= 0.35 * d_er + 1e-4, f"{what}: kernel-emulator RMS {d_ke:.3g} vs emulator-oracle RMS {d_er:.3g}"
+        entry.update(rms_kernel_emulator=d_ke, rms_emulator_oracle=d_er)
         msg += f"; RMS kernel-emulator {d_ke:.2e} vs emulator-exact {d_er:.2e}"
+    _record(entry)
     return msg
+
+
+def check_against_oracle(inp, got, glse, what, entry="prefill", num_splits=1, sched=None, emulate=True):
+    """The parity rule on every row of a small problem. got/glse: kernel output and LSE in the
+    output layouts. entry: "prefill" (one online softmax over each row's keys; the sink, if any,
+    at its end) or "decode" (num_splits split partials merged by the combine, which adds the sink).
+    sched: the emulator options of the entry point's documented schedule (tile_n, interleave,
+    granule), or None to skip the bug detector."""
+    rows = oracle.all_rows(inp)
+    o, l = gather(inp, np.asarray(got), np.asarray(glse), rows)
+    emu_d = emu_s = None
+    if emulate:
+        split = entry == "decode"
+        ns = num_splits if (split and inp.window_left < 0) else 1
+        stage = "combine" if split else "finalize"
+        emu_d = emulate_rows(inp, rows, tile_n=GRANULE, num_splits=ns, sink_stage=stage)
+        if sched is not None and not (split and inp.window_left >= 0 and num_splits > 1):
+            emu_s = emulate_rows(inp, rows, num_splits=num_splits if split else 1, sink_stage=stage, **sched)
+    return check_rows(inp, rows, o, l, what, emu_d, emu_s)

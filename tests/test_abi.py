@@ -178,35 +178,86 @@ def _paged_decode_args(b=64, hq=32, hkv=8, d=128, page=16, max_sk=8192):
     return q, k, v, kw
 
 
-def test_num_splits_for_picks_per_kernel(monkeypatch):
+def test_num_splits_for_picks_per_kernel():
     # paged GQA decode shape: the several-heads kernel has 64 x 2 one-wave units per split, so
     # 4 x 256 CUs / 128 = 8 splits; the per-head kernel has 64 x 8 units, 16 x 256 / 512 = 8
     q, k, v, kw = _paged_decode_args()
     assert binding.decode_num_splits_for(q, k, v, **kw) == 8
-    monkeypatch.setenv("FA8_DECODE_KERNEL", "lanes")
-    assert binding.decode_num_splits_for(q, k, v, **kw) == 8
-    monkeypatch.delenv("FA8_DECODE_KERNEL")
+    # the standalone helper is the per-head kernel's heuristic with one row block per kv head
+    assert binding.decode_num_splits(64, 8, 8192) == 8
     # long single-kv-head decode: capped at FA8_MAX_SPLITS, at least 4 granules per split
     q, k, v, kw = _paged_decode_args(b=4, hq=8, hkv=1, page=64, max_sk=131072)
     n = binding.decode_num_splits_for(q, k, v, **kw)
     assert 64 <= n <= binding.MAX_SPLITS
+    assert binding.decode_num_splits(4, 1, 131072) == n      # 8/1 heads: one row block, per-head kernel
     # short sequences: at least four 64-key granules per split
     q, k, v, kw = _paged_decode_args(b=1, max_sk=512)
     assert binding.decode_num_splits_for(q, k, v, **kw) == 2
+    assert binding.decode_num_splits(1, 8, 512) == 2
 
 
-def test_decode_plan(monkeypatch):
+def test_decode_plan():
     q, k, v, kw = _paged_decode_args()
     plan = binding.decode_plan(q, k, v, num_splits=16, **kw)
     # paged GQA decode (4 rows per kv head): 4 kv heads per wave fill its 16 MFMA rows, 16-key
     # steps, 64 batches x 2 head groups x 16 splits
     assert plan == dict(kernel=1, block_keys=16, key_groups=1, heads_per_workgroup=4, workgroups=64 * 2 * 16)
-    monkeypatch.setenv("FA8_DECODE_KERNEL", "lanes")
-    plan = binding.decode_plan(q, k, v, num_splits=16, **kw)
+    assert binding.decode_plan(q, k, v, num_splits=16, kernel=binding.DECODE_HEAD_GROUP, **kw) == plan
+    plan = binding.decode_plan(q, k, v, num_splits=16, kernel=binding.DECODE_PER_HEAD, **kw)
     assert plan == dict(kernel=0, block_keys=64, key_groups=1, heads_per_workgroup=1, workgroups=64 * 8 * 16)
-    monkeypatch.delenv("FA8_DECODE_KERNEL")
     with pytest.raises(binding.FA8Error):
         binding.decode_plan(q, k, v, num_splits=0, **kw)
+    with pytest.raises(binding.FA8Error) as e:
+        binding.decode_plan(q, k, v, num_splits=4, kernel=7, **kw)
+    assert e.value.status == binding.FA8_ERR_INVALID
+    # d = 96 has no several-heads kernel: asking for it is unsupported, the library's choice is not
+    q96, k96, v96 = (torch.zeros(t.shape[:-1] + (96,), dtype=torch.uint8) for t in (q, k, v))
+    with pytest.raises(binding.FA8Error) as e:
+        binding.decode_plan(q96, k96, v96, num_splits=4, kernel=binding.DECODE_HEAD_GROUP, **kw)
+    assert e.value.status == binding.FA8_ERR_UNSUPPORTED
+    assert binding.decode_plan(q96, k96, v96, num_splits=4, **kw)["kernel"] == 0
+
+
+def test_decode_ex_rejects_before_launch():
+    # the explicit-kernel entry point validates the choice before touching any pointer
+    lib = binding.load()
+    q, k, v, kw = _paged_decode_args()
+    p = binding._params(q, k, v, kw["cu_seqlens_q"], None, kw["seqused_k"], kw["block_table"], 1, 8192,
+                        None, None, None, 0.0, False, -1, -1)
+    assert lib.fa8_fwd_decode_splitkv_ex(ctypes.byref(p), 4, 5, None, None, None) == binding.FA8_ERR_INVALID
+    q96, k96, v96 = (torch.zeros(t.shape[:-1] + (96,), dtype=torch.uint8) for t in (q, k, v))
+    p = binding._params(q96, k96, v96, kw["cu_seqlens_q"], None, kw["seqused_k"], kw["block_table"], 1, 8192,
+                        None, None, None, 0.0, False, -1, -1)
+    assert lib.fa8_fwd_decode_splitkv_ex(ctypes.byref(p), 4, binding.DECODE_HEAD_GROUP, None, None,
+                                         None) == binding.FA8_ERR_UNSUPPORTED
+
+
+def test_prefill_grid_limit():
+    # a launch holds at most 2^32 - 1 threads along x: 2^24 workgroups of 256 threads. Varlen
+    # inputs deal 8 * ceil(B * Hkv / 8) groups x ceil(max_seqlen_q / 128) row blocks x g heads:
+    # 64 sequences of up to 512K tokens with 64/8 heads need exactly 2^24 and are rejected before
+    # any launch; half that length fits (host values only, nothing is read)
+    lib = binding.load()
+    b, hq, hkv, d = 64, 64, 8, 128
+
+    def status(max_sq):
+        q = torch.zeros((16, hq, d), dtype=torch.uint8)
+        k = torch.zeros((16, hkv, d), dtype=torch.uint8)
+        cu = torch.zeros(b + 1, dtype=torch.int32)
+        p = binding._params(q, k, k, cu, cu, None, None, max_sq, max_sq, None, None, None, 0.0, True, -1, -1)
+        binding._set_out(p, torch.zeros((16, hq, d), dtype=torch.bfloat16), None, True)
+        return lib.fa8_fwd_prefill(ctypes.byref(p), None)
+
+    # 8 * 64 * 4096 * 8 = 2^24 workgroups
+    assert status(512 * 1024) == binding.FA8_ERR_INVALID
+    assert "2^24" in binding.last_error()
+    # the same check without launching
+    q = torch.zeros((16, hq, d), dtype=torch.uint8)
+    k = torch.zeros((16, hkv, d), dtype=torch.uint8)
+    cu = torch.zeros(b + 1, dtype=torch.int32)
+    out = torch.zeros((16, hq, d), dtype=torch.bfloat16)
+    assert binding.check_params(q, k, k, cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=512 * 1024,
+                                max_seqlen_k=512 * 1024, causal=True, out=out) == binding.FA8_ERR_INVALID
 
 
 def test_quantize_q_host_validation():

@@ -31,15 +31,14 @@ def _shift(k, v, bt):
     return big_k, big_v, bt + pad
 
 
-def _decode_both(inp, monkeypatch, kernel):
-    if kernel == "lanes":
-        monkeypatch.setenv("FA8_DECODE_KERNEL", "lanes")
+def _decode_both(inp, kernel):
+    kern = binding.DECODE_PER_HEAD if kernel == "lanes" else binding.DECODE_AUTO
     q, k, v, kw = tensors(inp)
     res = []
     for pools in ((k, v, kw["block_table"]), _shift(k, v, kw["block_table"])):
         kk, vv, bt = pools
         args = dict(kw, block_table=bt)
-        out, lse = binding.decode(q, kk, vv, out_dtype=out_dtype(inp), return_lse=True, **args)
+        out, lse = binding.decode(q, kk, vv, out_dtype=out_dtype(inp), return_lse=True, kernel=kern, **args)
         torch.cuda.synchronize()
         res.append((out.float().cpu(), lse.cpu()))
         del kk, vv
@@ -48,18 +47,18 @@ def _decode_both(inp, monkeypatch, kernel):
 
 
 @pytest.mark.parametrize("kernel", ["heads", "lanes"])
-def test_paged_gqa_decode_pages_beyond_4gib(monkeypatch, kernel):
+def test_paged_gqa_decode_pages_beyond_4gib(kernel):
     inp = gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096)
     print(f"decode ({kernel} kernel), pages beyond 4 GiB: B{inp.batch} page {inp.page_size}", flush=True)
-    (o0, l0), (o1, l1) = _decode_both(inp, monkeypatch, kernel)
+    (o0, l0), (o1, l1) = _decode_both(inp, kernel)
     assert torch.isfinite(o0).all()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
 
 
-def test_long_pages_decode_pages_beyond_4gib(monkeypatch):
+def test_long_pages_decode_pages_beyond_4gib():
     inp = gen.long_kv_decode(3, batch=2, seqlen=8192)
     print(f"decode (64-token pages), pages beyond 4 GiB: B{inp.batch} Sk {inp.max_seqlen_k}", flush=True)
-    (o0, l0), (o1, l1) = _decode_both(inp, monkeypatch, "default")
+    (o0, l0), (o1, l1) = _decode_both(inp, "default")
     assert torch.isfinite(o0).all()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
 

@@ -62,4 +62,4 @@ def test_quantized_q_through_prefill():
     out, lse = binding.prefill(q, k, v, return_lse=True, **kw)
     torch.cuda.synchronize()
     print(check_against_oracle(inp, out.float().cpu().numpy(), lse.cpu().numpy(), "quantized q prefill",
-                               tile_n=prefill_tile(128, 128)), flush=True)
+                               sched=dict(tile_n=prefill_tile(128, 128))), flush=True)
