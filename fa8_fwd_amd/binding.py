@@ -105,6 +105,8 @@ def load():
     lib.fa8_fwd_decode_splitkv.argtypes = [P, i32, vp, vp, vp]
     lib.fa8_fwd_decode_splitkv_ex.argtypes = [P, i32, i32, vp, vp, vp]
     lib.fa8_fwd_decode_splitkv_ex.restype = ctypes.c_int
+    lib.fa8_fwd_decode_noalloc.argtypes = [P, i32, vp]
+    lib.fa8_fwd_decode_noalloc.restype = ctypes.c_int
     lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, vp]
     lib.fa8_check_params.argtypes = [P, i32]
     QP = ctypes.POINTER(QuantParams)
@@ -438,6 +440,25 @@ def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=tor
     combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=cu_q, lse=lse, sink=sink,
             stream=stream)
     return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def decode_noalloc(q, k, v, *, out: torch.Tensor, lse: Optional[torch.Tensor] = None, num_splits: int = 0,
+                   sink: Optional[torch.Tensor] = None, stream=None, **kw):
+    """Split-KV decode and combine in one call with the partials in the library's own scratch
+    (fa8_fwd_decode_noalloc): out (and lse) must be given, nothing is allocated."""
+    lib = load()
+    cu_q = kw.get("cu_seqlens_q")
+    p = _params(q, k, v, cu_q, kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
+                kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), kw.get("q_descale"), kw.get("k_descale"),
+                kw.get("v_descale"), kw.get("softmax_scale", 0.0), kw.get("causal", False), kw.get("window_left", -1),
+                kw.get("window_right", -1))
+    _set_out(p, out, lse, cu_q is not None)
+    p.sink = _sink_ptr(sink, p.heads_q)
+    _check(lib.fa8_fwd_decode_noalloc(ctypes.byref(p), num_splits, _stream(stream)))
+    return out
 
 
 def check_params(q, k, v, num_splits: int = 0, **kw) -> int:

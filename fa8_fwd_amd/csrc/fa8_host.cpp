@@ -417,6 +417,35 @@ fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, f
   return fa8_fwd_decode_splitkv_ex(p, num_splits, -1, o_partial, lse_partial, stream);
 }
 
+fa8_status fa8_fwd_decode_noalloc(const fa8_fwd_params* p, int32_t num_splits, void* stream) {
+  if (!p) return fail(FA8_ERR_INVALID, "params is NULL");
+  if (num_splits == 0) num_splits = fa8_decode_num_splits_for(p, 0);
+  if (num_splits < 1) return fail(FA8_ERR_INVALID, "num_splits must be >= 1, or 0 (got %d)", num_splits);
+  fa8_status st = validate(p, num_splits);
+  if (st != FA8_OK) return st;
+  if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
+  // the combine's output checks, before anything is launched
+  if (!p->out || !aligned(p->out, 8)) return fail(FA8_ERR_INVALID, "out must be non-NULL and 8-byte aligned");
+  const int64_t so[] = {p->o_row_stride, p->o_head_stride, p->cu_seqlens_q ? 0 : p->o_batch_stride};
+  for (int64_t s : so)
+    if (s < 0 || s % 4 != 0) return fail(FA8_ERR_INVALID, "out strides must be non-negative multiples of 4");
+  if (p->lse && !aligned(p->lse, 4)) return fail(FA8_ERR_INVALID, "lse must be 4-byte aligned");
+  const size_t need = fa8_decode_workspace_bytes(num_splits, p->batch, p->max_seqlen_q, p->heads_q, p->dv);
+  if (need == 0 || need > (size_t)FA8_NOALLOC_SCRATCH_BYTES)
+    return fail(FA8_ERR_INVALID, "the split partials need %zu bytes; the library's scratch holds %zu (fewer splits, "
+                "or fa8_fwd_decode_splitkv with caller buffers)", need, (size_t)FA8_NOALLOC_SCRATCH_BYTES);
+  void* base = nullptr;
+  hipError_t e = fa8::noalloc_scratch(&base);
+  if (e != hipSuccess) return fail(FA8_ERR_HIP, "cannot resolve the scratch address: %s", hipGetErrorString(e));
+  const size_t o_bytes = (size_t)num_splits * p->batch * p->max_seqlen_q * p->heads_q * p->dv * sizeof(float);
+  float* op = (float*)base;
+  float* lp = (float*)((uint8_t*)base + (o_bytes + 255) / 256 * 256);
+  if ((st = fa8_fwd_decode_splitkv(p, num_splits, op, lp, stream)) != FA8_OK) return st;
+  return fa8_combine(op, lp, num_splits, p->batch, p->max_seqlen_q, p->cu_seqlens_q, p->heads_q, p->dv, p->out,
+                     p->o_batch_stride, p->o_row_stride, p->o_head_stride, p->out_dtype, p->lse, p->lse_batch_stride,
+                     p->lse_head_stride, p->lse_row_stride, p->sink, stream);
+}
+
 fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t num_splits, int32_t batch,
                        int32_t max_seqlen_q, const int32_t* cu_seqlens_q, int32_t heads_q, int32_t dv, void* out,
                        int64_t o_batch_stride, int64_t o_row_stride, int64_t o_head_stride, int32_t out_dtype,

@@ -86,5 +86,8 @@ hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_prefill_mx(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_combine(const CParams& cp, hipStream_t stream);
+// Device address (on the current device) of the library's static scratch array of
+// FA8_NOALLOC_SCRATCH_BYTES bytes.
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace fa8

@@ -31,9 +31,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
+#include "fa8.h"
 #include "fa8_internal.h"
+
+// Split partials of fa8_fwd_decode_noalloc: one static array per GPU the library runs on, held
+// until the process ends. Host code never passes this name to a kernel (on the host it is only a
+// stand-in for the symbol): fa8::noalloc_scratch resolves the device address once per device.
+static __device__ __align__(256) uint8_t scratch[FA8_NOALLOC_SCRATCH_BYTES];
 
 namespace fa8 {
 
@@ -2196,6 +2203,28 @@ hipError_t launch_combine(const CParams& cp, hipStream_t stream) {
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(fa8_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, cp);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device, looked up with hipGetSymbolAddress the first
+// time a device asks (with that device current) and kept per device.
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa8

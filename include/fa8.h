@@ -176,6 +176,22 @@ fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);
 fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, float* o_partial,
                                   float* lse_partial, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split-KV decode and its combine in one call, writing
+ * p->out (and p->lse when set) exactly as fa8_fwd_decode_splitkv into caller buffers followed by
+ * fa8_combine would, with the split partials held in a scratch area the library owns: one static
+ * device array of FA8_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends. Nothing is
+ * allocated or freed. num_splits: 1 .. FA8_MAX_SPLITS, or 0 for fa8_decode_num_splits_for(p, 0).
+ * FA8_ERR_INVALID when the partials (fa8_decode_workspace_bytes) do not fit the scratch area,
+ * or for the argument errors of fa8_fwd_decode_splitkv and fa8_combine. Every call on one GPU
+ * uses the same scratch: calls that may overlap on one GPU (several streams, several threads)
+ * race and must be serialized by the caller. No part of the scratch needs clearing: every
+ * partial the combine reads is written by the decode first.
+ */
+#define FA8_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa8_status fa8_fwd_decode_noalloc(const fa8_fwd_params* p, int32_t num_splits, void* stream);
+
 /* Decode kernels fa8_fwd_decode_splitkv_ex can be asked for (fa8_decode_plan_info.kernel).
  * AUTO is the library's choice (what fa8_fwd_decode_splitkv uses). PER_HEAD takes every problem.
  * HEAD_GROUP (several kv heads per wave, whole token rows) takes (d, dv) = (64, 64) or
