@@ -1,14 +1,15 @@
 """Benchmark of the FP8 attention forward on one MI355X.
 
-One step = one split-KV decode pass plus its combine over the paged GQA decode workload
-(64 sequences, 32 query / 8 KV heads, d = 128, one query token, 16-token pages, lengths
-uniform in [1024, 8192], per-(batch, kv head) descales): the headline value is its whole-step
-K+V bandwidth in GB/s. The causal-prefill workload (B = 2, 8192 x 8192, 32/8 heads, d = 128)
-is timed next to it and reported in TFLOP/s under "prefill".
+One step = one split-KV decode step over the paged GQA decode workload (64 sequences, 32 query
+/ 8 KV heads, d = 128, one query token, 16-token pages, lengths uniform in [1024, 8192],
+per-(batch, kv head) descales): the device-computed balanced split schedule, the decode pass and
+the combine, captured in a HIP graph and replayed, as the pages time decode. The headline value
+is the step's K+V bandwidth in GB/s. The causal-prefill workload (B = 2, 8192 x 8192, 32/8
+heads, d = 128) is timed next to it and reported in TFLOP/s under "prefill".
 
 Prints one JSON line. Inputs are resident in HBM before timing; the dominant kernel's own
-duration is measured with HIP events on its launch stream inside the timed region (around the
-decode kernel of every tenth timed step: an event pair on every step would add about 5% to it).
+duration is measured with HIP events on its launch stream around the decode kernel of every step
+of an eager loop.
 """
 from __future__ import annotations
 
@@ -143,111 +144,135 @@ def device_args(inp, dev):
     return to_dev(inp.q, dev), to_dev(inp.k, dev), to_dev(inp.v, dev), kw
 
 
-EVENT_EVERY = 10
+# Decode steps captured in one HIP graph: a model's forward replays its attention layers inside one
+# graph, back to back; the launch gap of a graph replay comes once per forward, not per layer.
+STEPS_PER_GRAPH = 8
 
 
-def bench_decode(inp, steps: int, warmup: int, dev, num_splits=None, event_every: int = EVENT_EVERY):
+def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced", num_splits=None):
+    """One decode step of `path`:
+      "balanced": fa8_fwd_decode_scheduled (which derives the per-request split schedule on the
+                  device) + fa8_combine_scheduled;
+      "static":   fa8_fwd_decode_splitkv with the library's split count + fa8_combine.
+    Three timings, with the inputs resident in HBM:
+      graph_ms: STEPS_PER_GRAPH steps captured once in a HIP graph and replayed until `steps`
+                steps have run, wall time / steps (the pages time decode as the per-layer
+                attention span of replayed CUDA graphs); the replays' output must equal the eager
+                step's bit for bit;
+      eager_ms: the same calls issued eagerly, wall time / steps;
+      kernel_ms: HIP events on the launch stream around the decode kernel of every step of the
+                eager loop (mean; median and quartiles beside it).
+    Returns a dict."""
     q, k, v, kw = device_args(inp, dev)
     B, HQ, SQ, DV = inp.batch, inp.heads_q, inp.max_seqlen_q, inp.dv
-    S = num_splits or binding.decode_num_splits_for(q, k, v, **kw)
-    op = torch.empty((S, B, SQ, HQ, DV), dtype=torch.float32, device=dev)
-    lp = torch.empty((S, B, SQ, HQ), dtype=torch.float32, device=dev)
     out = torch.empty((q.shape[0], HQ, DV), dtype=torch.bfloat16, device=dev)
+    cu = kw["cu_seqlens_q"]
+    if path == "balanced":
+        W = binding.decode_num_workers(q, k, v, **kw)
+        sched = torch.empty(int(binding.load().fa8_decode_schedule_bytes(B)) // 4, dtype=torch.int32, device=dev)
+        op = torch.empty((W + B, SQ, HQ, DV), dtype=torch.float32, device=dev)
+        lp = torch.empty((W + B, SQ, HQ), dtype=torch.float32, device=dev)
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record()
-        binding.decode_splitkv(q, k, v, num_splits=S, o_partial=op, lse_partial=lp, **kw)
-        if evs is not None:
-            evs[1].record()
-        binding.combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=kw["cu_seqlens_q"])
+        def pre():
+            pass
+
+        def decode():
+            binding.decode_scheduled(q, k, v, num_workers=W, schedule=sched, o_partial=op, lse_partial=lp, **kw)
+
+        def post():
+            binding.combine_scheduled(op, lp, sched, num_workers=W, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV,
+                                      out=out, cu_seqlens_q=cu)
+        count = {"num_workers": W}
+    else:
+        S = num_splits or binding.decode_num_splits_for(q, k, v, **kw)
+        op = torch.empty((S, B, SQ, HQ, DV), dtype=torch.float32, device=dev)
+        lp = torch.empty((S, B, SQ, HQ), dtype=torch.float32, device=dev)
+
+        def pre():
+            pass
+
+        def decode():
+            binding.decode_splitkv(q, k, v, num_splits=S, o_partial=op, lse_partial=lp, **kw)
+
+        def post():
+            binding.combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=cu)
+        count = {"num_splits": S}
+
+    def step():
+        pre()
+        decode()
+        post()
 
     for _ in range(warmup):
         step()
-    # HIP events around the decode kernel of every event_every-th timed step (an event pair on
-    # every step adds about 6 us to a 120 us step; one in ten adds under 1 us), not the first
-    # timed step, which starts on an idle GPU
-    sampled = list(range(min(event_every // 2, steps - 1), steps, event_every))
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs.get(i))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs.values()]))
-    assert torch.isfinite(out.float()).all(), "non-finite decode output"
-    return (t1 - t0) * 1e3 / steps, kernel_ms, S
-
-
-def bench_decode_graph(inp, steps: int, warmup: int, dev, num_splits=None):
-    """Decode step (decode + combine) captured once in a HIP graph and replayed `steps` times,
-    timed by HIP events around the replays: a short decode kernel leaves the eager step bound by
-    the host's launch calls. The kernel time comes from HIP events around the decode kernel on
-    every step of an eager loop before the capture. Returns (graph step ms, eager step ms,
-    kernel ms, splits); every replay's output must equal the eager one bit for bit."""
-    q, k, v, kw = device_args(inp, dev)
-    B, HQ, SQ, DV = inp.batch, inp.heads_q, inp.max_seqlen_q, inp.dv
-    S = num_splits or binding.decode_num_splits_for(q, k, v, **kw)
-    op = torch.empty((S, B, SQ, HQ, DV), dtype=torch.float32, device=dev)
-    lp = torch.empty((S, B, SQ, HQ), dtype=torch.float32, device=dev)
-    out = torch.empty((q.shape[0], HQ, DV), dtype=torch.bfloat16, device=dev)
-
-    def decode():
-        binding.decode_splitkv(q, k, v, num_splits=S, o_partial=op, lse_partial=lp, **kw)
-
-    def combine():
-        binding.combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=kw["cu_seqlens_q"])
-
-    for _ in range(warmup):
-        decode()
-        combine()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in evs:
+        pre()
         a.record()
         decode()
         b.record()
-        combine()
+        post()
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kt = np.array([a.elapsed_time(b) for a, b in evs])
     ref = out.clone()
+    assert torch.isfinite(ref.float()).all(), "non-finite decode output"
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        decode()
-        combine()
+        step()
     torch.cuda.current_stream().wait_stream(side)
     with torch.cuda.graph(graph):
-        decode()
-        combine()
-    for _ in range(warmup):
+        for _ in range(STEPS_PER_GRAPH):
+            step()
+    replays = max(1, -(-steps // STEPS_PER_GRAPH))
+    for _ in range(max(1, warmup // STEPS_PER_GRAPH)):
         graph.replay()
-    reps = 4 * steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
+    t0 = time.perf_counter()
+    for _ in range(replays):
         graph.replay()
-    e1.record()
     torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / (replays * STEPS_PER_GRAPH)
     assert torch.equal(out, ref), "graph replay differs from the eager decode step"
-    return e0.elapsed_time(e1) / reps, eager_ms, kernel_ms, S
+    res = dict(count, graph_ms=graph_ms, eager_ms=eager_ms, kernel_ms=float(kt.mean()),
+               kernel_ms_median=float(np.median(kt)), kernel_ms_q1=float(np.percentile(kt, 25)),
+               kernel_ms_q3=float(np.percentile(kt, 75)))
+    del graph
+    return res
 
 
-def decode_kernel_name(inp, dev, num_splits: int) -> str:
+def decode_kernel_name(inp, dev, balanced: bool) -> str:
     """Name of the decode kernel the library's plan picks for this workload."""
     q, k, v, kw = device_args(inp, dev)
-    plan = binding.decode_plan(q, k, v, num_splits=num_splits, **kw)
+    plan = binding.decode_plan(q, k, v, num_splits=1, **kw)
     paged = inp.block_table is not None
+    how = "balanced schedule" if balanced else "static splits"
     if plan["kernel"] == 1:
         step_page = (not paged) or inp.page_size >= plan["block_keys"]
-        return (f"fa8_decode_heads_kernel<{inp.d},{inp.dv},{plan['heads_per_workgroup']},{int(paged)},{int(step_page)}>"
-                f" (split-KV decode, {plan['heads_per_workgroup']} kv heads per wave, {plan['workgroups']} waves)")
-    return f"fa8_decode_kernel<{inp.d},{inp.dv},...> (split-KV decode, one kv head per wave, {plan['workgroups']} waves)"
+        return (f"fa8_decode_heads_kernel<{inp.d},{inp.dv},{plan['heads_per_workgroup']},{int(paged)},{int(step_page)},"
+                f"{int(balanced)}> (split-KV decode, {plan['heads_per_workgroup']} kv heads per wave, {how})")
+    return f"fa8_decode_kernel<{inp.d},{inp.dv},...,{int(balanced)}> (split-KV decode, one kv head per wave, {how})"
+
+
+def decode_figures(inp, r: dict) -> dict:
+    """GB/s of a bench_decode_step result: the step (graph-replayed and eager) on the step's
+    algorithmic bytes, the kernel on the kernel's."""
+    sb, kb = decode_step_bytes(inp), decode_kernel_bytes(inp)
+    gbs = lambda nbytes, ms: round(nbytes / (ms * 1e-3) / 1e9, 2)
+    d = {k: v for k, v in r.items() if k in ("num_workers", "num_splits")}
+    d.update(step_value=gbs(sb, r["graph_ms"]), step_ms=round(r["graph_ms"], 5),
+             step_timing=f"decode (with its split schedule) and combine, {STEPS_PER_GRAPH} steps per HIP graph, "
+                         f"replayed back to back",
+             eager_step_value=gbs(sb, r["eager_ms"]), eager_step_ms=round(r["eager_ms"], 5),
+             kernel_value=gbs(kb, r["kernel_ms"]), kernel_ms=round(r["kernel_ms"], 5),
+             kernel_ms_median=round(r["kernel_ms_median"], 5),
+             kernel_ms_quartiles=[round(r["kernel_ms_q1"], 5), round(r["kernel_ms_q3"], 5)],
+             kernel_pct_of_hbm_peak=round(100 * kb / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))
+    return d
 
 
 def bench_prefill(inp, steps: int, warmup: int, dev):
@@ -293,25 +318,20 @@ def bench_prefill_mx(inp, steps: int, warmup: int, dev):
 
 def other_workloads(args, dev) -> dict:
     """Figures of the remaining measured workloads, reported beside the headline (not part of
-    `value`): long-KV decode (4 sequences of 131072 keys, 8/1 heads, 64-token pages; GB/s of the
-    decode step, as a replayed HIP graph and eager, and of its kernel), the causal prefill workload with a learnable sink, the Q
-    quantizer, the MXFP8 prefill on the causal prefill shape, and the mixed-shape varlen prefill
-    (8 sequences, window 1024, fp16 out; TFLOP/s of the visible pairs) for (d, dv) = (256, 256)
-    and (192, 128)."""
+    `value`): the paged GQA decode with the static splits of fa8_fwd_decode_splitkv; long-KV
+    decode (4 sequences of 131072 keys, 8/1 heads, 64-token pages; GB/s of the decode step, as a
+    replayed HIP graph and eager, and of its kernel) on both paths; the causal prefill workload
+    with a learnable sink, the Q quantizer, the MXFP8 prefill on the causal prefill shape, and the
+    mixed-shape varlen prefill (8 sequences, window 1024, fp16 out; TFLOP/s of the visible pairs)
+    for (d, dv) = (256, 256) and (192, 128)."""
     out = {}
+    dec = gen.paged_gqa_decode(1)
+    st = bench_decode_step(dec, args.steps, args.warmup // 2, dev, "static", args.num_splits or None)
+    out["paged_gqa_decode_static_splits"] = dict(workload=dec.name, unit="GB/s", **decode_figures(dec, st))
     lk = gen.long_kv_decode(3)
-    # its decode kernel runs about 30 us, shorter than the host's launch calls of an eager step:
-    # the step is timed as a replayed HIP graph (the eager figure beside it), the kernel by HIP
-    # events around every decode launch of the eager loop
-    gms, ems, kms, S = bench_decode_graph(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev)
-    kb = decode_kernel_bytes(lk)
-    sb = decode_step_bytes(lk)
-    out["long_kv_decode"] = {"workload": lk.name, "num_splits": S, "unit": "GB/s",
-                             "step_value": round(sb / (gms * 1e-3) / 1e9, 2), "step_ms": round(gms, 5),
-                             "step_timing": "decode + combine captured in one HIP graph, replayed",
-                             "eager_step_value": round(sb / (ems * 1e-3) / 1e9, 2),
-                             "kernel_value": round(kb / (kms * 1e-3) / 1e9, 2), "kernel_ms": round(kms, 5),
-                             "kernel_pct_of_hbm_peak": round(100 * kb / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    for path in ("balanced", "static"):
+        r = bench_decode_step(lk, max(10, args.steps // 2), max(10, args.warmup // 2), dev, path)
+        out[f"long_kv_decode_{path}"] = dict(workload=lk.name, unit="GB/s", **decode_figures(lk, r))
     # the causal prefill workload with a learnable sink logit per query head (N(0, 1))
     cs = gen.with_sink(gen.causal_prefill(2), 12)
     ms, kms = bench_prefill(cs, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
@@ -441,7 +461,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=50)
-    ap.add_argument("--num-splits", type=int, default=0, help="0 = the library's heuristic")
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="static splits of the paged GQA decode figure beside the headline (0 = the library's heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-KV decode and mixed varlen figures")
@@ -463,19 +484,20 @@ def main():
         copy_calibration(args.calibrate_copy, dev)
 
     dec = gen.paged_gqa_decode(1)
-    ms_step, kern_ms, S = bench_decode(dec, args.steps, args.warmup, dev, args.num_splits or None)
+    r = bench_decode_step(dec, args.steps, args.warmup, dev, "balanced")
+    fig = decode_figures(dec, r)
     step_bytes = decode_step_bytes(dec)
     kbytes = decode_kernel_bytes(dec)
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kbytes / (kern_ms * 1e-3) / 1e9
+    value = fig["step_value"]
+    achieved = fig["kernel_value"]
     line = {
         "metric": "FP8 attn fwd TFLOP/s (prefill) & decode HBM GB/s, % of MI355X peak",
-        "value": round(value, 2),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": fig["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -483,13 +505,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": dec.name, "batch": dec.batch, "heads_q": dec.heads_q, "heads_kv": dec.heads_kv,
                    "d": dec.d, "page_size": dec.page_size, "seqlens_k": "uniform [1024, 8192], seed 1",
-                   "sum_seqlen_k": int(dec.seqlens_k().sum()), "num_splits": S, "out": "bf16",
-                   "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
-        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(dec, dev, S),
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "sum_seqlen_k": int(dec.seqlens_k().sum()), "num_workers": r["num_workers"],
+                   "split_schedule": "balanced (device-computed per-request splits)", "out": "bf16",
+                   "step_bytes": step_bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "step_timing": fig["step_timing"], "eager_step_value": fig["eager_step_value"],
+                   "eager_step_ms": fig["eager_step_ms"]},
+        "roofline": {"bound": "hbm", "kernel": decode_kernel_name(dec, dev, True),
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"fa8_decode_heads_kernel_{dec.name}_traffic.md"),
-                     "kernel_ms": round(kern_ms, 5), "bytes_per_launch": kbytes},
+                     "traffic": recorded_traffic(f"fa8_decode_heads_kernel_balanced_{dec.name}_traffic.md"),
+                     "kernel_ms": fig["kernel_ms"], "kernel_ms_median": fig["kernel_ms_median"],
+                     "kernel_ms_quartiles": fig["kernel_ms_quartiles"], "bytes_per_launch": kbytes},
     }
     if not args.no_prefill:
         pre = gen.causal_prefill(2)

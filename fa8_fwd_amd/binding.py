@@ -107,6 +107,19 @@ def load():
     lib.fa8_fwd_decode_splitkv_ex.restype = ctypes.c_int
     lib.fa8_fwd_decode_noalloc.argtypes = [P, i32, vp]
     lib.fa8_fwd_decode_noalloc.restype = ctypes.c_int
+    lib.fa8_decode_schedule_bytes.argtypes = [i32]
+    lib.fa8_decode_schedule_bytes.restype = ctypes.c_size_t
+    lib.fa8_decode_scheduled_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa8_decode_scheduled_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa8_decode_num_workers.argtypes = [P, i32]
+    lib.fa8_decode_num_workers.restype = i32
+    lib.fa8_decode_schedule.argtypes = [P, i32, vp, vp]
+    lib.fa8_decode_schedule.restype = ctypes.c_int
+    lib.fa8_fwd_decode_scheduled.argtypes = [P, i32, vp, i32, vp, vp, vp]
+    lib.fa8_fwd_decode_scheduled.restype = ctypes.c_int
+    lib.fa8_combine_scheduled.argtypes = [vp, vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64,
+                                          i64, i64, vp, vp]
+    lib.fa8_combine_scheduled.restype = ctypes.c_int
     lib.fa8_combine.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, vp, i64, i64, i64, i32, vp, i64, i64, i64, vp, vp]
     lib.fa8_check_params.argtypes = [P, i32]
     QP = ctypes.POINTER(QuantParams)
@@ -439,6 +452,93 @@ def decode(q, k, v, *, num_splits: Optional[int] = None, out=None, out_dtype=tor
         lse = _alloc_out(q, DV, out.dtype, varlen, True, B, HQ, SQ)[1] if return_lse else None
     combine(op, lp, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV, out=out, cu_seqlens_q=cu_q, lse=lse, sink=sink,
             stream=stream)
+    return (out, lse) if return_lse else out
+
+
+MAX_WORKERS = 65535
+
+
+def _decode_params(q, k, v, kw):
+    return _params(q, k, v, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"), kw.get("seqused_k"), kw.get("block_table"),
+                   kw.get("max_seqlen_q"), kw.get("max_seqlen_k"), kw.get("q_descale"), kw.get("k_descale"),
+                   kw.get("v_descale"), kw.get("softmax_scale", 0.0), kw.get("causal", False),
+                   kw.get("window_left", -1), kw.get("window_right", -1))
+
+
+def decode_num_workers(q, k, v, *, cu_count: int = 0, **kw) -> int:
+    """Workers of the balanced decode the library picks for this problem (fa8_decode_num_workers)."""
+    return int(load().fa8_decode_num_workers(ctypes.byref(_decode_params(q, k, v, kw)), cu_count))
+
+
+def decode_schedule(q, k, v, *, num_workers: int, schedule: Optional[torch.Tensor] = None, stream=None, **kw):
+    """Writes the balanced decode schedule (fa8_decode_schedule) into `schedule` (int32, allocated
+    when None) and returns it."""
+    lib = load()
+    p = _decode_params(q, k, v, kw)
+    if schedule is None:
+        schedule = torch.empty(int(lib.fa8_decode_schedule_bytes(p.batch)) // 4, dtype=torch.int32, device=q.device)
+    if schedule.dtype != torch.int32 or not schedule.is_contiguous():
+        raise FA8Error(FA8_ERR_INVALID, "schedule must be a contiguous int32 tensor")
+    if schedule.numel() * 4 < int(lib.fa8_decode_schedule_bytes(p.batch)):
+        raise FA8Error(FA8_ERR_INVALID, "schedule buffer too small")
+    _check(lib.fa8_decode_schedule(ctypes.byref(p), num_workers, schedule.data_ptr(), _stream(stream)))
+    return schedule
+
+
+def decode_scheduled(q, k, v, *, num_workers: int, schedule: torch.Tensor, o_partial=None, lse_partial=None,
+                     kernel: int = DECODE_AUTO, stream=None, **kw):
+    """Partials of the balanced decode (fa8_fwd_decode_scheduled), which also writes the schedule
+    into `schedule`: o_partial [W + B, Sq, Hq, dv] and lse_partial [W + B, Sq, Hq] fp32."""
+    lib = load()
+    p = _decode_params(q, k, v, kw)
+    slots = num_workers + p.batch
+    if o_partial is None:
+        o_partial = torch.empty((slots, p.max_seqlen_q, p.heads_q, p.dv), dtype=torch.float32, device=q.device)
+    if lse_partial is None:
+        lse_partial = torch.empty((slots, p.max_seqlen_q, p.heads_q), dtype=torch.float32, device=q.device)
+    if o_partial.numel() < slots * p.max_seqlen_q * p.heads_q * p.dv or lse_partial.numel() < slots * p.max_seqlen_q * p.heads_q:
+        raise FA8Error(FA8_ERR_INVALID, "partial buffers too small")
+    _check(lib.fa8_fwd_decode_scheduled(ctypes.byref(p), num_workers, schedule.data_ptr(), kernel, o_partial.data_ptr(),
+                                        lse_partial.data_ptr(), _stream(stream)))
+    return o_partial, lse_partial
+
+
+def combine_scheduled(o_partial, lse_partial, schedule, *, num_workers: int, batch: int, max_seqlen_q: int,
+                      heads_q: int, dv: int, out: torch.Tensor, cu_seqlens_q=None, lse: Optional[torch.Tensor] = None,
+                      sink: Optional[torch.Tensor] = None, stream=None):
+    """Merge of the balanced decode's partials (fa8_combine_scheduled)."""
+    lib = load()
+    varlen = cu_seqlens_q is not None
+    if out.dtype not in _OUT:
+        raise FA8Error(FA8_ERR_INVALID, "out must be bfloat16 or float16")
+    ob, orow, oh = (0, out.stride(0), out.stride(1)) if varlen else (out.stride(0), out.stride(1), out.stride(2))
+    lb = lh = lr = 0
+    if lse is not None:
+        lb, lh, lr = (0, lse.stride(0), lse.stride(1)) if varlen else (lse.stride(0), lse.stride(1), lse.stride(2))
+    _check(lib.fa8_combine_scheduled(o_partial.data_ptr(), lse_partial.data_ptr(), schedule.data_ptr(), num_workers,
+                                     batch, max_seqlen_q, _ptr(cu_seqlens_q), heads_q, dv, out.data_ptr(), ob, orow,
+                                     oh, _OUT[out.dtype], _ptr(lse), lb, lh, lr, _sink_ptr(sink, heads_q),
+                                     _stream(stream)))
+    return out
+
+
+def decode_balanced(q, k, v, *, num_workers: Optional[int] = None, out=None, out_dtype=torch.bfloat16,
+                    return_lse=False, sink: Optional[torch.Tensor] = None, kernel: int = DECODE_AUTO, stream=None, **kw):
+    """Balanced split-KV decode: partials (with their schedule), then the combine. num_workers=None
+    uses fa8_decode_num_workers."""
+    p = _decode_params(q, k, v, kw)
+    if num_workers is None:
+        num_workers = int(load().fa8_decode_num_workers(ctypes.byref(p), 0))
+    sched = torch.empty(int(load().fa8_decode_schedule_bytes(p.batch)) // 4, dtype=torch.int32, device=q.device)
+    op, lp = decode_scheduled(q, k, v, num_workers=num_workers, schedule=sched, kernel=kernel, stream=stream, **kw)
+    cu_q = kw.get("cu_seqlens_q")
+    varlen = cu_q is not None
+    if out is None:
+        out, lse = _alloc_out(q, p.dv, out_dtype, varlen, return_lse, p.batch, p.heads_q, p.max_seqlen_q)
+    else:
+        lse = _alloc_out(q, p.dv, out.dtype, varlen, True, p.batch, p.heads_q, p.max_seqlen_q)[1] if return_lse else None
+    combine_scheduled(op, lp, sched, num_workers=num_workers, batch=p.batch, max_seqlen_q=p.max_seqlen_q,
+                      heads_q=p.heads_q, dv=p.dv, out=out, cu_seqlens_q=cu_q, lse=lse, sink=sink, stream=stream)
     return (out, lse) if return_lse else out
 
 

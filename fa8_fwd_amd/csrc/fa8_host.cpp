@@ -417,6 +417,91 @@ fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, f
   return fa8_fwd_decode_splitkv_ex(p, num_splits, -1, o_partial, lse_partial, stream);
 }
 
+// ---- balanced decode schedule ----
+size_t fa8_decode_schedule_bytes(int32_t batch) {
+  if (batch < 0) return 0;
+  return (size_t)(2 + 2 * ((int64_t)batch + 1)) * sizeof(int32_t);
+}
+
+size_t fa8_decode_scheduled_workspace_bytes(int32_t num_workers, int32_t batch, int32_t max_seqlen_q, int32_t heads_q,
+                                            int32_t dv) {
+  if (num_workers < 1 || batch < 0) return 0;
+  return fa8_decode_workspace_bytes((int32_t)std::min<int64_t>((int64_t)num_workers + batch, INT32_MAX), 1,
+                                    max_seqlen_q, heads_q, dv);
+}
+
+int32_t fa8_decode_num_workers(const fa8_fwd_params* p, int32_t cu_count) {
+  if (!p || validate(p, 1) != FA8_OK) return 1;
+  if (p->batch <= 0 || p->heads_kv <= 0 || p->max_seqlen_k <= 0 || p->max_seqlen_q <= 0) return 1;
+  fa8::KParams k = make_kparams(p);
+  k.nmb = 1;
+  if (cu_count <= 0) cu_count = 256;
+  const int64_t units = std::max(1, fa8::decode_units_per_worker(k, p->d, p->dv));
+  // about one wave per SIMD for either kernel (equal shares leave no idle tail to fill, and more
+  // concurrent streams measured slower); the segments cut at sequence ends add up to batch more
+  const int64_t target = (int64_t)cu_count * kHeadsWavesPerCu;
+  // at least four granules per worker on average when every sequence is max_seqlen_k long
+  const int64_t granules = (int64_t)p->batch * (((int64_t)p->max_seqlen_k + FA8_SPLIT_GRANULE - 1) / FA8_SPLIT_GRANULE);
+  int64_t w = (target + units - 1) / units;
+  w = std::min<int64_t>(w, std::max<int64_t>(1, granules / 4));
+  w = std::min<int64_t>(w, FA8_MAX_WORKERS - p->batch);
+  return (int32_t)std::max<int64_t>(1, w);
+}
+
+namespace {
+fa8_status validate_scheduled(const fa8_fwd_params* p, int32_t num_workers) {
+  fa8_status st = validate(p, 1);
+  if (st != FA8_OK) return st;
+  if (num_workers < 1 || (int64_t)num_workers + p->batch > FA8_MAX_WORKERS)
+    return fail(FA8_ERR_INVALID, "num_workers %d outside 1 .. %d - batch", num_workers, FA8_MAX_WORKERS);
+  if ((int64_t)p->max_seqlen_q * (p->heads_kv > 0 ? p->heads_q / p->heads_kv : 0) > fa8::kDecodeRows)
+    return fail(FA8_ERR_UNSUPPORTED, "the balanced decode schedule takes at most %d packed rows per kv head "
+                "(max_seqlen_q x heads_q / heads_kv)", fa8::kDecodeRows);
+  return FA8_OK;
+}
+}  // namespace
+
+fa8_status fa8_decode_schedule(const fa8_fwd_params* p, int32_t num_workers, int32_t* schedule, void* stream) {
+  fa8_status st = validate_scheduled(p, num_workers);
+  if (st != FA8_OK) return st;
+  if (!schedule || !aligned(schedule, 4)) return fail(FA8_ERR_INVALID, "schedule must be non-NULL and 4-byte aligned");
+  if (p->batch == 0) return ok();
+  if (validate_env() && (st = validate_device_data(p, stream)) != FA8_OK) return st;
+  fa8::KParams k = make_kparams(p);
+  hipError_t e = fa8::launch_decode_schedule(k, num_workers, schedule, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA8_ERR_HIP, "schedule launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fa8_status fa8_fwd_decode_scheduled(const fa8_fwd_params* p, int32_t num_workers, int32_t* schedule,
+                                    int32_t kernel, float* o_partial, float* lse_partial, void* stream) {
+  fa8_status st = validate_scheduled(p, num_workers);
+  if (st != FA8_OK) return st;
+  fa8::KParams k = make_kparams(p);
+  k.decode_kernel = decode_kernel_for(k, p, kernel, &st);
+  if (st != FA8_OK) return st;
+  if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
+  if (!schedule || !aligned(schedule, 4)) return fail(FA8_ERR_INVALID, "schedule must be non-NULL and 4-byte aligned");
+  if (!o_partial || !lse_partial) return fail(FA8_ERR_INVALID, "o_partial and lse_partial must be non-NULL");
+  if (!aligned(o_partial, 16) || !aligned(lse_partial, 4))
+    return fail(FA8_ERR_INVALID, "o_partial must be 16-byte aligned and lse_partial 4-byte aligned");
+  k.o_part = o_partial;
+  k.lse_part = lse_partial;
+  k.nmb = 1;
+  k.sched = schedule;
+  k.sched_out = schedule;
+  k.sched_workers = num_workers;
+  if (p->heads_kv >= kMaxDecodeGridX) return fail(FA8_ERR_INVALID, "decode grid too large");
+  // up to 64 sequences every wave derives the schedule from the lengths itself (and the first
+  // writes it for the combine); beyond, the schedule kernel writes it first
+  k.sched_inline = p->batch <= 64 ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (!k.sched_inline) e = fa8::launch_decode_schedule(k, num_workers, schedule, (hipStream_t)stream);
+  if (e == hipSuccess) e = fa8::launch_decode_sched(k, p->d, p->dv, num_workers, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA8_ERR_HIP, "scheduled decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 fa8_status fa8_fwd_decode_noalloc(const fa8_fwd_params* p, int32_t num_splits, void* stream) {
   if (!p) return fail(FA8_ERR_INVALID, "params is NULL");
   if (num_splits == 0) num_splits = fa8_decode_num_splits_for(p, 0);
@@ -446,6 +531,27 @@ fa8_status fa8_fwd_decode_noalloc(const fa8_fwd_params* p, int32_t num_splits, v
                      p->lse_head_stride, p->lse_row_stride, p->sink, stream);
 }
 
+namespace {
+fa8_status combine_impl(const float* o_partial, const float* lse_partial, const int32_t* sched, int32_t num_splits,
+                        int32_t batch, int32_t max_seqlen_q, const int32_t* cu_seqlens_q, int32_t heads_q, int32_t dv,
+                        void* out, int64_t o_batch_stride, int64_t o_row_stride, int64_t o_head_stride,
+                        int32_t out_dtype, float* lse, int64_t lse_batch_stride, int64_t lse_head_stride,
+                        int64_t lse_row_stride, const float* sink, void* stream);
+}  // namespace
+
+fa8_status fa8_combine_scheduled(const float* o_partial, const float* lse_partial, const int32_t* schedule,
+                                 int32_t num_workers, int32_t batch, int32_t max_seqlen_q, const int32_t* cu_seqlens_q,
+                                 int32_t heads_q, int32_t dv, void* out, int64_t o_batch_stride, int64_t o_row_stride,
+                                 int64_t o_head_stride, int32_t out_dtype, float* lse, int64_t lse_batch_stride,
+                                 int64_t lse_head_stride, int64_t lse_row_stride, const float* sink, void* stream) {
+  if (num_workers < 1 || (int64_t)num_workers + batch > FA8_MAX_WORKERS)
+    return fail(FA8_ERR_INVALID, "num_workers %d outside 1 .. %d - batch", num_workers, FA8_MAX_WORKERS);
+  if (!schedule || !aligned(schedule, 4)) return fail(FA8_ERR_INVALID, "schedule must be non-NULL and 4-byte aligned");
+  return combine_impl(o_partial, lse_partial, schedule, num_workers, batch, max_seqlen_q, cu_seqlens_q, heads_q, dv,
+                      out, o_batch_stride, o_row_stride, o_head_stride, out_dtype, lse, lse_batch_stride,
+                      lse_head_stride, lse_row_stride, sink, stream);
+}
+
 fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t num_splits, int32_t batch,
                        int32_t max_seqlen_q, const int32_t* cu_seqlens_q, int32_t heads_q, int32_t dv, void* out,
                        int64_t o_batch_stride, int64_t o_row_stride, int64_t o_head_stride, int32_t out_dtype,
@@ -453,6 +559,19 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
                        const float* sink, void* stream) {
   if (num_splits < 1 || num_splits > FA8_MAX_SPLITS)
     return fail(FA8_ERR_INVALID, "num_splits %d outside 1..%d", num_splits, FA8_MAX_SPLITS);
+  return combine_impl(o_partial, lse_partial, nullptr, num_splits, batch, max_seqlen_q, cu_seqlens_q, heads_q, dv, out,
+                      o_batch_stride, o_row_stride, o_head_stride, out_dtype, lse, lse_batch_stride, lse_head_stride,
+                      lse_row_stride, sink, stream);
+}
+
+}  // extern "C"
+
+namespace {
+fa8_status combine_impl(const float* o_partial, const float* lse_partial, const int32_t* sched, int32_t num_splits,
+                        int32_t batch, int32_t max_seqlen_q, const int32_t* cu_seqlens_q, int32_t heads_q, int32_t dv,
+                        void* out, int64_t o_batch_stride, int64_t o_row_stride, int64_t o_head_stride,
+                        int32_t out_dtype, float* lse, int64_t lse_batch_stride, int64_t lse_head_stride,
+                        int64_t lse_row_stride, const float* sink, void* stream) {
   if (batch < 0 || max_seqlen_q < 0 || heads_q < 0 || max_seqlen_q >= kMaxLen || heads_q >= 65536 || batch >= 65536)
     return fail(FA8_ERR_INVALID, "bad sizes (batch %d, max_seqlen_q %d, heads_q %d)", batch, max_seqlen_q, heads_q);
   if (dv != 64 && dv != 96 && dv != 128 && dv != 192 && dv != 256)
@@ -473,12 +592,12 @@ fa8_status fa8_combine(const float* o_partial, const float* lse_partial, int32_t
   c.out_fp16 = out_dtype == FA8_OUT_FP16;
   c.lse = lse; c.l_bs = lse_batch_stride; c.l_hs = lse_head_stride; c.l_rs = lse_row_stride;
   c.sink = sink;
+  c.sched = sched;
   hipError_t e = fa8::launch_combine(c, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA8_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
   return ok();
 }
-
-}  // extern "C"
+}  // namespace
 
 // ---- Q quantizer ----
 namespace {

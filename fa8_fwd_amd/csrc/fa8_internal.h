@@ -34,6 +34,10 @@ struct KParams {
   int32_t bk8;                // prefill with per-sequence lengths: ceil(batch * hkv / 8), else 0
   const float* sink;          // [hq] sink logits or null (prefill finalize only)
   int32_t decode_kernel;      // -1: the library's choice; 0: per-head kernel; 1: several heads per wave
+  const int32_t* sched;       // balanced decode schedule (fa8_decode_schedule), or null for static splits
+  int32_t* sched_out;         // the schedule buffer the decode waves write when they compute it
+  int32_t sched_inline;       // 1: every wave computes the schedule itself (batch <= 64)
+  int32_t sched_workers;      // W of the balanced schedule
   // MXFP8 block scales (E8M0 bytes; strides in bytes), MX prefill only
   const uint8_t* q_mx; int64_t qmx_bs, qmx_rs, qmx_hs;
   const uint8_t* k_mx; int64_t kmx_bs, kmx_rs, kmx_hs;
@@ -49,6 +53,7 @@ struct CParams {
   int32_t o_vec16;            // out 16-byte aligned, its strides multiples of 8 elements
   float* lse; int64_t l_bs, l_hs, l_rs;
   const float* sink;          // [hq] sink logits or null
+  const int32_t* sched;       // balanced decode schedule (partial slots per sequence), or null
 };
 
 // Q quantizer: one chunk = kQuantRows rows of one (batch, kv head) block.
@@ -79,12 +84,17 @@ constexpr int kKvTile = 64;
 // cannot take it; and the same subject to kp.decode_kernel (0 when the per-head kernel is used).
 int decode_heads_applicable(const KParams& kp, int d, int dv);
 int decode_heads_choice(const KParams& kp, int d, int dv);
-// Workgroups per split of the decode kernel launch_decode picks.
+// Workgroups per split of the decode kernel launch_decode picks; per worker of a balanced schedule.
 int decode_units_per_split(const KParams& kp, int d, int dv);
+int decode_units_per_worker(const KParams& kp, int d, int dv);
 
 hipError_t launch_prefill(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_prefill_mx(const KParams& kp, int d, int dv, hipStream_t stream);
 hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream);
+// Balanced schedule: fa8_decode_schedule_kernel, then the decode kernels with one wave per
+// (kv head unit, worker); kp.sched set, one row block per kv head.
+hipError_t launch_decode_schedule(const KParams& kp, int32_t workers, int32_t* sched, hipStream_t stream);
+hipError_t launch_decode_sched(const KParams& kp, int d, int dv, int32_t workers, hipStream_t stream);
 hipError_t launch_combine(const CParams& cp, hipStream_t stream);
 // Device address (on the current device) of the library's static scratch array of
 // FA8_NOALLOC_SCRATCH_BYTES bytes.

@@ -280,6 +280,144 @@ __device__ __forceinline__ SeqInfo seq_info(const KParams& p, int b) {
   return s;
 }
 
+// The same lengths for a lane's own b (b may differ between lanes).
+__device__ __forceinline__ SeqInfo seq_info_lane(const KParams& p, int b) {
+  SeqInfo s;
+  s.q0 = p.cu_q ? p.cu_q[b] : 0;
+  s.sq = p.cu_q ? p.cu_q[b + 1] - s.q0 : p.max_sq;
+  if (p.used_k) s.sk = p.used_k[b];
+  else if (p.cu_k) s.sk = p.cu_k[b + 1] - p.cu_k[b];
+  else s.sk = p.max_sk;
+  return s;
+}
+
+// Keys seen by the query rows i_first .. i_last of one sequence: their union [lo, hi) and the
+// range [full_lo, full_hi) every one of them sees (tiles inside it need no mask); an empty union
+// is [0, 0).
+struct DecodeKeys {
+  int lo, hi, full_lo, full_hi;
+};
+__device__ __forceinline__ DecodeKeys decode_keys(const RowRange& rr, int i_first, int i_last) {
+  DecodeKeys k{0, 0, 0, 0};
+  if (i_last >= i_first) {
+    k.lo = rr.lo(i_first);
+    k.hi = rr.hi(i_last);
+    k.full_lo = rr.lo(i_last);
+    k.full_hi = rr.hi(i_first);
+  }
+  if (k.hi <= k.lo) { k.lo = 0; k.hi = 0; }
+  return k;
+}
+// Granules (of kKvTile keys, counted from key 0) [g0, g1) that hold the union of a decode
+// block's keys: g0 = lo / kKvTile, g1 = ceil(hi / kKvTile); none for an empty union.
+__device__ __forceinline__ int union_granule0(const DecodeKeys& k) { return k.lo / kKvTile; }
+__device__ __forceinline__ int union_granules(const DecodeKeys& k) {
+  return k.hi > k.lo ? (k.hi + kKvTile - 1) / kKvTile - k.lo / kKvTile : 0;
+}
+// Static split s of S over a decode block's n granules: [g0 + floor(s n / S), g0 + floor((s+1) n / S)).
+__device__ __forceinline__ void split_range(const DecodeKeys& k, int split, int nsplit, int& s0, int& s1) {
+  const int g0 = union_granule0(k), n = union_granules(k);
+  s0 = g0 + (int)(((int64_t)split * n) / nsplit);
+  s1 = g0 + (int)(((int64_t)(split + 1) * n) / nsplit);
+}
+
+// Balanced decode schedule (written by fa8_decode_schedule_kernel): sched[0] = G, the granules
+// of all sequences; sched[1] = W, the workers; gst = sched + 2 holds the exclusive prefix of the
+// sequences' granule counts ([batch + 1] entries), pst = gst + batch + 1 the exclusive prefix of
+// their segment counts. Worker w of W takes global granules [floor(w G / W), floor((w+1) G / W));
+// global granule x belongs to worker owner(x) = floor(((x + 1) W - 1) / G). A segment is one
+// (sequence, worker) pair whose granules meet; segment j of sequence b (pst[b] <= j < pst[b+1])
+// is that of worker owner(gst[b]) + j - pst[b], and j is also its partial slot.
+__device__ __forceinline__ int sched_owner(int x, int W, int G) { return (int)(((int64_t)(x + 1) * W - 1) / G); }
+// Segment j from the schedule computed by the wave itself (at most 64 sequences: lane b holds
+// sequence b), the same integers fa8_decode_schedule_kernel writes; the first wave of the grid
+// also writes them to the schedule buffer for the combine.
+__device__ __forceinline__ bool sched_segment_inline(const KParams& p, int j, int& b, int& gs0, int& gs1) {
+  const int lane = threadIdx.x & 63;
+  const int W = p.sched_workers;
+  int v = 0, g0 = 0;
+  if (lane < p.batch) {
+    const SeqInfo si = seq_info_lane(p, lane);
+    const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+    const DecodeKeys k = decode_keys(rr, 0, si.sq - 1);
+    v = union_granules(k);
+    g0 = union_granule0(k);
+  }
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  const int G = __builtin_amdgcn_readlane(incl, 63);
+  const int gst = incl - v;
+  const int n = (v > 0) ? sched_owner(gst + v - 1, W, G) - sched_owner(gst, W, G) + 1 : 0;
+  int nincl = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(nincl, o);
+    if (lane >= o) nincl += u;
+  }
+  const int pst = nincl - n;
+  const int nseg = __builtin_amdgcn_readlane(nincl, 63);
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    int32_t* out = p.sched_out;
+    if (lane == 0) {
+      out[0] = G;
+      out[1] = W;
+      out[2 + p.batch] = G;
+      out[3 + 2 * p.batch] = nseg;
+    }
+    if (lane < p.batch) {
+      out[2 + lane] = gst;
+      out[3 + p.batch + lane] = pst;
+    }
+  }
+  if (j >= nseg) return false;
+  // the last b with pst[b] <= j (pst nondecreasing over lanes 0 .. batch-1, pst[0] = 0)
+  const int cnt = __popcll(__builtin_amdgcn_ballot_w64(lane < p.batch && pst <= j));
+  b = cnt - 1;
+  const int gb0 = __builtin_amdgcn_readlane(gst, b), gv = __builtin_amdgcn_readlane(v, b);
+  const int w = sched_owner(gb0, W, G) + (j - __builtin_amdgcn_readlane(pst, b));
+  const int A = (int)(((int64_t)w * G) / W), Z = (int)(((int64_t)(w + 1) * G) / W);
+  const int sg0 = __builtin_amdgcn_readlane(g0, b);
+  gs0 = sg0 + max(A, gb0) - gb0;
+  gs1 = sg0 + min(Z, gb0 + gv) - gb0;
+  return true;
+}
+
+// Segment j: its sequence b and granules [gs0, gs1) of that sequence (absolute, counted from its
+// key 0); false when j is past the last segment. Wave-uniform.
+__device__ __forceinline__ bool sched_segment(const KParams& p, int j, int& b, int& gs0, int& gs1) {
+  if (p.sched_inline) return sched_segment_inline(p, j, b, gs0, gs1);
+  const int32_t* gst = p.sched + 2;
+  const int32_t* pst = gst + p.batch + 1;
+  if (j >= __builtin_amdgcn_readfirstlane(pst[p.batch])) return false;
+  const int G = __builtin_amdgcn_readfirstlane(p.sched[0]);
+  const int W = __builtin_amdgcn_readfirstlane(p.sched[1]);
+  // the last b with pst[b] <= j (pst[0] = 0, nondecreasing, pst[batch] > j), by a 64-way search
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = p.batch;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool le = idx < hi && pst[idx] <= j;
+    const int cnt = __popcll(__builtin_amdgcn_ballot_w64(le));   // lanes 0 .. cnt-1 (monotone), cnt >= 1
+    lo = lo + (cnt - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  b = lo;
+  const int gb0 = __builtin_amdgcn_readfirstlane(gst[b]), gb1 = __builtin_amdgcn_readfirstlane(gst[b + 1]);
+  const int w = sched_owner(gb0, W, G) + (j - __builtin_amdgcn_readfirstlane(pst[b]));
+  const int A = (int)(((int64_t)w * G) / W), Z = (int)(((int64_t)(w + 1) * G) / W);
+  const SeqInfo si = seq_info(p, b);
+  const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+  const int g0 = union_granule0(decode_keys(rr, 0, si.sq - 1));
+  gs0 = g0 + max(A, gb0) - gb0;
+  gs1 = g0 + min(Z, gb1) - gb0;
+  return true;
+}
+
 // Element offsets of K/V row j of (batch b, kv head kvh).
 struct KvAddr {
   const int32_t* trow;   // block-table row, or null
@@ -1271,9 +1409,12 @@ constexpr int decode_depth() {
   return 2;
 }
 
-template <int D, int DV, int NQB, int PAGEMODE>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-fa8_decode_kernel(const KParams p) {
+// One (batch b, kv head kvh, row block mblock) of the per-head decode over the keys of granules
+// [gs0, gs1) of sequence b (intersected with the block's visible keys), or, when !SCHED, over
+// those of static split `ga` (gb unused); the partial goes to partial slot `slot`.
+template <int D, int DV, int NQB, int PAGEMODE, bool SCHED>
+__device__ __forceinline__ void perhead_segment(const KParams& p, int b, int kvh, int mblock, int ga, int gb,
+                                                int64_t slot, uint8_t* smem) {
   constexpr int DEPTH = decode_depth<D, DV, NQB>();
   constexpr int BN = kKvTile;
   constexpr int KCH = D / 16, VCH = DV / 16;
@@ -1281,15 +1422,11 @@ fa8_decode_kernel(const KParams p) {
   constexpr int KPT = KCH, VPT = VCH;        // 16-byte chunks per lane per tile (64 rows x NCH / 64)
   constexpr int KS = (D + 127) / 128;
   constexpr int NB = DV / 16;
-  constexpr int BM = 32;                     // rows of a decode block (NQB * 16 of them are computed)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[KTILE + VTILE];
+  constexpr int BM = kDecodeRows;            // rows of a decode block (NQB * 16 of them are computed)
+  static_assert(BN == kKvTile, "granules are KV tiles");
 
   const int lane = threadIdx.x;
   const int h4 = lane >> 4, l16 = lane & 15;
-  const int b = blockIdx.z;
-  const int split = blockIdx.y;
-  const int kvh = blockIdx.x / p.nmb;
-  const int mblock = blockIdx.x - kvh * p.nmb;
   const int g = p.g;
 
   const SeqInfo si = seq_info(p, b);
@@ -1299,19 +1436,11 @@ fa8_decode_kernel(const KParams p) {
   const int rb1 = min(rb0 + BM, rows_total) - 1;
   const int i_first = rb0 / g, i_last = rb1 / g;
   const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
-  int wg_lo = rr.lo(i_first), wg_hi = rr.hi(i_last);
-  int full_lo = rr.lo(i_last), full_hi = rr.hi(i_first);
-  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
-  {
-    // split s covers granules [g0 + s*n/S, g0 + (s+1)*n/S) of the block's granule range
-    const int g0 = wg_lo / BN, g1 = (wg_hi + BN - 1) / BN, n = g1 - g0;
-    const int s0 = g0 + (int)(((int64_t)split * n) / p.nsplit);
-    const int s1 = g0 + (int)(((int64_t)(split + 1) * n) / p.nsplit);
-    wg_lo = max(wg_lo, s0 * BN);
-    wg_hi = min(wg_hi, s1 * BN);
-    full_lo = max(full_lo, s0 * BN);
-    full_hi = min(full_hi, s1 * BN);
-  }
+  const DecodeKeys dk0 = decode_keys(rr, i_first, i_last);
+  int gs0 = ga, gs1 = gb;
+  if constexpr (!SCHED) split_range(dk0, ga, p.nsplit, gs0, gs1);
+  const int wg_lo = max(dk0.lo, gs0 * BN), wg_hi = min(dk0.hi, gs1 * BN);
+  const int full_lo = max(dk0.full_lo, gs0 * BN), full_hi = min(dk0.full_hi, gs1 * BN);
   const int t_begin = wg_lo / BN;
   const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
 
@@ -1527,7 +1656,7 @@ fa8_decode_kernel(const KParams p) {
     const bool nonempty = l_tot > 0.0f;
     const float inv = nonempty ? dvs / l_tot : 0.0f;
     const float lse = nonempty ? (m_run[qb] + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
-    const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi[qb]) * p.hq + qh[qb];
+    const int64_t prow = (slot * p.max_sq + qi[qb]) * p.hq + qh[qb];
     float* orow = p.o_part + prow * DV;
 #pragma unroll
     for (int n = 0; n < NB; n++) {
@@ -1535,6 +1664,23 @@ fa8_decode_kernel(const KParams p) {
       *reinterpret_cast<v4f*>(orow + 16 * n + 4 * h4) = v;
     }
     if (h4 == 0) p.lse_part[prow] = lse;
+  }
+}
+
+// One wave per (kv head, row block, split, batch) with static splits, or per (kv head, segment) of
+// a balanced schedule (SCHED; one row block per kv head).
+template <int D, int DV, int NQB, int PAGEMODE, bool SCHED>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+fa8_decode_kernel(const KParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kKvTile * (D + DV)];
+  if constexpr (SCHED) {
+    int b, s0, s1;
+    if (!sched_segment(p, blockIdx.y, b, s0, s1)) return;
+    perhead_segment<D, DV, NQB, PAGEMODE, true>(p, b, blockIdx.x, 0, s0, s1, blockIdx.y, smem);
+  } else {
+    const int b = blockIdx.z, split = blockIdx.y;
+    const int kvh = blockIdx.x / p.nmb, mblock = blockIdx.x - kvh * p.nmb;
+    perhead_segment<D, DV, NQB, PAGEMODE, false>(p, b, kvh, mblock, split, 0, (int64_t)split * p.batch + b, smem);
   }
 }
 
@@ -1554,9 +1700,20 @@ fa8_decode_kernel(const KParams p) {
 // ------------------------------------------------------------------------------------------
 // PAGED: K/V through the block table; STEP_PAGE: page_size >= BN, so each step's rows lie in
 // one page (or K/V are contiguous) and one descriptor per step serves all of its loads.
-template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa8_decode_heads_kernel(const KParams p) {
+template <int D, int DV, int HPW>
+struct HeadsGeom {
+  static constexpr int KB = 4 / HPW, BN = 16 * KB;
+  static constexpr int KR = HPW * D, VR = HPW * DV;
+  static constexpr int SMEM = BN * KR + BN * VR;
+};
+
+// One (batch b, kv heads kvh0 .. kvh0 + HPW - 1) of the several-heads decode over the keys of
+// granules [ra, rb) of sequence b (intersected with the rows' visible keys), or, when !SCHED,
+// over those of static split `ra`; the partial goes to partial slot `slot` (rows
+// slot * max_seqlen_q * heads_q + i * heads_q + h).
+template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE, bool SCHED>
+__device__ __forceinline__ void heads_segment(const KParams& p, int b, int kvh0, int ra, int rb, int64_t slot,
+                                              uint8_t* smem) {
   static_assert(HPW == 2 || HPW == 4, "two or four kv heads per wave");
   constexpr int KB = 4 / HPW;                        // 16-key blocks per step
   constexpr int BN = 16 * KB;                        // keys per step
@@ -1570,35 +1727,20 @@ fa8_decode_heads_kernel(const KParams p) {
   constexpr int KS = (D + 127) / 128;
   constexpr int NB = DV / 16;
   constexpr int DEPTH = 1;   // one register stage + the LDS stage; two waves per SIMD overlap
-  __shared__ __attribute__((aligned(16))) uint8_t smem[KTILE + VTILE];
+  static_assert(HeadsGeom<D, DV, HPW>::SMEM == KTILE + VTILE, "LDS size");
 
   const int lane = threadIdx.x;
   const int kg = lane >> 4, l16 = lane & 15;
-  const int b = blockIdx.z, split = blockIdx.y;
-  const int kvh0 = blockIdx.x * HPW;
   const int g = p.g;
   const SeqInfo si = seq_info(p, b);
   const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
 
-  // ---- key range of the wave (all query tokens of the batch) and of this split ----
-  int wg_lo = 0, wg_hi = 0, full_lo = 0, full_hi = 0;
-  if (si.sq > 0) {
-    wg_lo = rr.lo(0);
-    wg_hi = rr.hi(si.sq - 1);
-    full_lo = rr.lo(si.sq - 1);
-    full_hi = rr.hi(0);
-  }
-  if (wg_hi <= wg_lo) { wg_lo = 0; wg_hi = 0; }
-  {
-    // split s covers granules [g0 + s*n/S, g0 + (s+1)*n/S) of the block's granule range
-    const int g0 = wg_lo / kKvTile, g1 = (wg_hi + kKvTile - 1) / kKvTile, n = g1 - g0;
-    const int s0 = g0 + (int)(((int64_t)split * n) / p.nsplit);
-    const int s1 = g0 + (int)(((int64_t)(split + 1) * n) / p.nsplit);
-    wg_lo = max(wg_lo, s0 * kKvTile);
-    wg_hi = min(wg_hi, s1 * kKvTile);
-    full_lo = max(full_lo, s0 * kKvTile);
-    full_hi = min(full_hi, s1 * kKvTile);
-  }
+  // ---- key range of the wave (all query tokens of the batch), cut to the given granules ----
+  const DecodeKeys dk0 = decode_keys(rr, 0, si.sq - 1);
+  int gs0 = ra, gs1 = rb;
+  if constexpr (!SCHED) split_range(dk0, ra, p.nsplit, gs0, gs1);
+  const int wg_lo = max(dk0.lo, gs0 * kKvTile), wg_hi = min(dk0.hi, gs1 * kKvTile);
+  const int full_lo = max(dk0.full_lo, gs0 * kKvTile), full_hi = min(dk0.full_hi, gs1 * kKvTile);
   const int t_begin = wg_lo / BN;
   const int t_end = wg_hi > wg_lo ? (wg_hi + BN - 1) / BN : t_begin;
 
@@ -1903,7 +2045,7 @@ fa8_decode_heads_kernel(const KParams p) {
   const bool nonempty = l_tot > 0.0f;
   const float inv = nonempty ? dvs / l_tot : 0.0f;
   const float lse = nonempty ? (m_run + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
-  const int64_t prow = (((int64_t)split * p.batch + b) * p.max_sq + qi) * p.hq + qh;
+  const int64_t prow = (slot * p.max_sq + qi) * p.hq + qh;
   float* orow = p.o_part + prow * DV;
 #pragma unroll
   for (int n = 0; n < NB; n++) {
@@ -1911,6 +2053,126 @@ fa8_decode_heads_kernel(const KParams p) {
     *reinterpret_cast<v4f*>(orow + 16 * n + 4 * kg) = v;
   }
   if (kg == 0) p.lse_part[prow] = lse;
+}
+
+// One wave per (group of HPW kv heads, split, batch) with static splits (split s of a sequence
+// covers granules [g0 + floor(s n / S), g0 + floor((s + 1) n / S)) of its n visible granules), or
+// per (group, segment) of a balanced schedule (SCHED; sched_segment).
+template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE, bool SCHED>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa8_decode_heads_kernel(const KParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[HeadsGeom<D, DV, HPW>::SMEM];
+  if constexpr (SCHED) {
+    int b, s0, s1;
+    if (!sched_segment(p, blockIdx.y, b, s0, s1)) return;
+    heads_segment<D, DV, HPW, PAGED, STEP_PAGE, true>(p, b, blockIdx.x * HPW, s0, s1, blockIdx.y, smem);
+  } else {
+    const int b = blockIdx.z, split = blockIdx.y;
+    heads_segment<D, DV, HPW, PAGED, STEP_PAGE, false>(p, b, blockIdx.x * HPW, split, 0,
+                                                       (int64_t)split * p.batch + b, smem);
+  }
+}
+
+// Inclusive prefix sum of v over the 1024 threads of a workgroup; *total receives the sum of all.
+__device__ __forceinline__ int block_scan1024(int v, int* total, int* s_w) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  __syncthreads();   // s_w is free (a previous call's readers are done)
+  if (lane == 63) s_w[wv] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int t = s_w[k];
+    before += (k < wv) ? t : 0;
+    all += t;
+  }
+  *total = all;
+  return v + before;
+}
+
+// Writes the balanced decode schedule (layout at sched_segment) for W workers: one workgroup of
+// 1024 threads, sequences in chunks of 1024. Sequence b's granules are those of the union of its
+// rows' visible keys (the granules a static split would share out); its partial slots are the
+// workers its granules meet.
+__global__ void __launch_bounds__(1024) fa8_decode_schedule_kernel(const KParams p, int32_t W, int32_t* sched) {
+  __shared__ int s_w[16];
+  int32_t* gst = sched + 2;
+  int32_t* pst = gst + p.batch + 1;
+  auto granules = [&](int b) -> int {
+    if (b >= p.batch) return 0;
+    const SeqInfo si = seq_info_lane(p, b);
+    const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
+    return union_granules(decode_keys(rr, 0, si.sq - 1));
+  };
+  // pass 1: granule prefix and G; with at most 1024 sequences the lengths are read once and the
+  // segment prefix follows in the same pass
+  const int b0 = (int)threadIdx.x;
+  const int v0 = granules(b0);
+  int tot0;
+  const int excl0 = block_scan1024(v0, &tot0, s_w) - v0;
+  if (b0 < p.batch) gst[b0] = excl0;
+  int G = tot0;
+  for (int base = 1024; base < p.batch; base += 1024) {
+    const int b = base + (int)threadIdx.x;
+    const int v = granules(b);
+    int tot;
+    const int incl = block_scan1024(v, &tot, s_w);
+    if (b < p.batch) gst[b] = G + incl - v;
+    G += tot;
+  }
+  // pass 2: segments per sequence and their prefix
+  auto segments = [&](int gb0, int v) { return v > 0 ? sched_owner(gb0 + v - 1, W, G) - sched_owner(gb0, W, G) + 1 : 0; };
+  const int n0 = segments(excl0, v0);
+  int ntot0;
+  const int nexcl0 = block_scan1024(n0, &ntot0, s_w) - n0;
+  if (b0 < p.batch) pst[b0] = nexcl0;
+  int gcarry = tot0, pcarry = ntot0;
+  for (int base = 1024; base < p.batch; base += 1024) {
+    const int b = base + (int)threadIdx.x;
+    const int v = granules(b);
+    int tot, ntot;
+    const int gb0 = gcarry + block_scan1024(v, &tot, s_w) - v;
+    const int n = segments(gb0, v);
+    const int nincl = block_scan1024(n, &ntot, s_w);
+    if (b < p.batch) pst[b] = pcarry + nincl - n;
+    gcarry += tot;
+    pcarry += ntot;
+  }
+  if (threadIdx.x == 0) {
+    sched[0] = G;
+    sched[1] = W;
+    gst[p.batch] = G;
+    pst[p.batch] = pcarry;
+  }
+}
+
+// The partial rows one output row (b, i, h) merges: static splits s = 0 .. nsplit-1 at row
+// (s * batch + b) * max_sq * hq + i * hq + h; with a balanced schedule the slots pst[b] ..
+// pst[b+1]-1 at row slot * max_sq * hq + i * hq + h.
+struct PartialRows {
+  int n;
+  int64_t first, stride;
+  __device__ int64_t at(int s) const { return first + (int64_t)s * stride; }
+};
+__device__ __forceinline__ PartialRows partial_rows(const CParams& c, int b, int i, int h, int64_t row, int64_t rows) {
+  PartialRows r;
+  if (c.sched) {
+    const int32_t* pst = c.sched + 2 + c.batch + 1;
+    const int p0 = pst[b];
+    r.n = pst[b + 1] - p0;
+    r.stride = (int64_t)c.max_sq * c.hq;
+    r.first = (int64_t)p0 * r.stride + (int64_t)i * c.hq + h;
+  } else {
+    r.n = c.nsplit;
+    r.first = row;
+    r.stride = rows;
+  }
+  return r;
 }
 
 // Log-sum-exp merge of split partials: one thread per 4 output elements of one row.
@@ -1927,6 +2189,7 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   const int q0 = c.cu_q ? c.cu_q[b] : 0;
   const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
   if (i >= sq) return;
+  const PartialRows pr = partial_rows(c, b, i, h, row, rows);
   // One pass over the splits in batches of 8 whose LSE and partial loads are all issued before
   // any is used (the kernel is bound by memory latency, not bandwidth): a running max, with the
   // sums rescaled when a batch raises it, so a problem of up to 8 splits costs one round trip.
@@ -1936,15 +2199,15 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   float mx = z;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float den = (z == kNegInf) ? 0.0f : 1.0f;          // e^(z - mx) with mx = z
-  for (int s0 = 0; s0 < c.nsplit; s0 += SB) {
+  for (int s0 = 0; s0 < pr.n; s0 += SB) {
     float ls[SB];
     v4f o[SB];
 #pragma unroll
     for (int k = 0; k < SB; k++) {
-      const bool in = s0 + k < c.nsplit;
-      ls[k] = in ? c.lse_part[(int64_t)(s0 + k) * rows + row] : kNegInf;
-      o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)(s0 + k) * rows + row) * c.dv + 4 * q)
-                : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      const bool in = s0 + k < pr.n;
+      const int64_t pi = pr.at(s0 + k);
+      ls[k] = in ? c.lse_part[pi] : kNegInf;
+      o[k] = in ? *reinterpret_cast<const v4f*>(c.o_part + pi * c.dv + 4 * q) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     }
     float bm = mx;
 #pragma unroll
@@ -1997,22 +2260,23 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
   const int q0 = c.cu_q ? c.cu_q[b] : 0;
   const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
   if (i >= sq) return;   // uniform over the workgroup
+  const PartialRows pr = partial_rows(c, b, i, h, row, rows);
   // one pass per split lane: a running maximum rescales the lane's weight sum and accumulator
   // whenever a batch of LSEs raises it, so every partial is read once
   float mx = kNegInf, den = 0.0f;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const bool has_cols = q < tpr;
-  for (int s0 = sp; s0 < c.nsplit; s0 += SB * SP) {
+  for (int s0 = sp; s0 < pr.n; s0 += SB * SP) {
     float ls[SB];
     v4f o[SB];
 #pragma unroll
     for (int k = 0; k < SB; k++) {
       const int sidx = s0 + k * SP;
-      const bool in = sidx < c.nsplit;
-      ls[k] = in ? c.lse_part[(int64_t)sidx * rows + row] : kNegInf;
-      o[k] = (in && has_cols)
-                 ? *reinterpret_cast<const v4f*>(c.o_part + ((int64_t)sidx * rows + row) * c.dv + 4 * q)
-                 : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      const bool in = sidx < pr.n;
+      const int64_t pi = pr.at(sidx);
+      ls[k] = in ? c.lse_part[pi] : kNegInf;
+      o[k] = (in && has_cols) ? *reinterpret_cast<const v4f*>(c.o_part + pi * c.dv + 4 * q)
+                              : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     }
     float bm = mx;
 #pragma unroll
@@ -2080,32 +2344,46 @@ static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {
                        stream, kp);
   return hipGetLastError();
 }
-template <int D, int DV, int NQB>
+template <int D, int DV, int NQB, int PAGEMODE, bool SCHED>
+static void launch_decode_k(const KParams& kp, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, PAGEMODE, SCHED>), grid, dim3(64), 0, stream, kp);
+}
+template <int D, int DV, int NQB, bool SCHED>
 static void launch_decode_q(const KParams& kp, dim3 grid, hipStream_t stream) {
   // the rows of one 64-lane load instruction (64 / (d/16) rows) lie in one page
   constexpr int rows_k = (64 % (D / 16) == 0) ? 64 / (D / 16) : 1 << 30;
   constexpr int rows_v = (64 % (DV / 16) == 0) ? 64 / (DV / 16) : 1 << 30;
   if (kp.page_shift < 0) {
-    hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 0>), grid, dim3(64), 0, stream, kp);
+    launch_decode_k<D, DV, NQB, 0, SCHED>(kp, grid, stream);
     return;
   }
   if constexpr (rows_k < (1 << 30) && rows_v < (1 << 30)) {
     if ((1 << kp.page_shift) >= rows_k && (1 << kp.page_shift) >= rows_v) {
-      hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 1>), grid, dim3(64), 0, stream, kp);
+      launch_decode_k<D, DV, NQB, 1, SCHED>(kp, grid, stream);
       return;
     }
   }
-  hipLaunchKernelGGL((fa8_decode_kernel<D, DV, NQB, 2>), grid, dim3(64), 0, stream, kp);
+  launch_decode_k<D, DV, NQB, 2, SCHED>(kp, grid, stream);
+}
+// static splits: (kv head x row block, split, batch); balanced schedule: (kv head, worker, 1)
+template <int D, int DV, bool SCHED>
+static hipError_t launch_decode_tt(const KParams& kp, hipStream_t stream) {
+  const dim3 grid = SCHED ? dim3((unsigned)kp.hkv, (unsigned)kp.nsplit, 1u)
+                          : dim3((unsigned)(kp.hkv * kp.nmb), (unsigned)kp.nsplit, (unsigned)kp.batch);
+  // blocks hold min(32, Sq * g) rows: one 16-row MFMA block suffices up to 16
+  if ((int64_t)kp.max_sq * kp.g <= 16)
+    launch_decode_q<D, DV, 1, SCHED>(kp, grid, stream);
+  else
+    launch_decode_q<D, DV, 2, SCHED>(kp, grid, stream);
+  return hipGetLastError();
 }
 template <int D, int DV>
 static hipError_t launch_decode_t(const KParams& kp, hipStream_t stream) {
-  dim3 grid((unsigned)(kp.hkv * kp.nmb), (unsigned)kp.nsplit, (unsigned)kp.batch);
-  // blocks hold min(32, Sq * g) rows: one 16-row MFMA block suffices up to 16
-  if ((int64_t)kp.max_sq * kp.g <= 16)
-    launch_decode_q<D, DV, 1>(kp, grid, stream);
-  else
-    launch_decode_q<D, DV, 2>(kp, grid, stream);
-  return hipGetLastError();
+  return launch_decode_tt<D, DV, false>(kp, stream);
+}
+template <int D, int DV>
+static hipError_t launch_decode_sched_t(const KParams& kp, hipStream_t stream) {
+  return launch_decode_tt<D, DV, true>(kp, stream);
 }
 
 #define FA8_DISPATCH(FN, d, dv, kp, stream)                                   \
@@ -2157,8 +2435,13 @@ int decode_heads_choice(const KParams& kp, int d, int dv) {
 
 template <int D, int DV, int HPW, bool PAGED, bool STEP_PAGE>
 static hipError_t launch_heads_t(const KParams& kp, hipStream_t stream) {
-  dim3 grid((unsigned)(kp.hkv / HPW), (unsigned)kp.nsplit, (unsigned)kp.batch);
-  hipLaunchKernelGGL((fa8_decode_heads_kernel<D, DV, HPW, PAGED, STEP_PAGE>), grid, dim3(64), 0, stream, kp);
+  if (kp.sched) {
+    const dim3 grid((unsigned)(kp.hkv / HPW), (unsigned)kp.nsplit, 1u);
+    hipLaunchKernelGGL((fa8_decode_heads_kernel<D, DV, HPW, PAGED, STEP_PAGE, true>), grid, dim3(64), 0, stream, kp);
+  } else {
+    const dim3 grid((unsigned)(kp.hkv / HPW), (unsigned)kp.nsplit, (unsigned)kp.batch);
+    hipLaunchKernelGGL((fa8_decode_heads_kernel<D, DV, HPW, PAGED, STEP_PAGE, false>), grid, dim3(64), 0, stream, kp);
+  }
   return hipGetLastError();
 }
 
@@ -2179,7 +2462,17 @@ hipError_t launch_decode(const KParams& kp, int d, int dv, hipStream_t stream) {
     FA8_HEADS_CASE(128, 4)
     return hipErrorInvalidValue;
   }
+  if (kp.sched) FA8_DISPATCH(launch_decode_sched_t, d, dv, kp, stream);
   FA8_DISPATCH(launch_decode_t, d, dv, kp, stream);
+}
+hipError_t launch_decode_sched(const KParams& kp, int d, int dv, int32_t workers, hipStream_t stream) {
+  KParams k = kp;
+  k.nsplit = workers + kp.batch;   // grid.y: one wave per possible segment (at most W + batch)
+  return launch_decode(k, d, dv, stream);
+}
+hipError_t launch_decode_schedule(const KParams& kp, int32_t workers, int32_t* sched, hipStream_t stream) {
+  hipLaunchKernelGGL(fa8_decode_schedule_kernel, dim3(1), dim3(1024), 0, stream, kp, workers, sched);
+  return hipGetLastError();
 }
 
 int decode_units_per_split(const KParams& kp, int d, int dv) {
@@ -2187,11 +2480,18 @@ int decode_units_per_split(const KParams& kp, int d, int dv) {
   if (hpw) return kp.batch * (kp.hkv / hpw);
   return kp.batch * kp.hkv * kp.nmb;
 }
+int decode_units_per_worker(const KParams& kp, int d, int dv) {
+  const int hpw = decode_heads_choice(kp, d, dv);
+  return hpw ? kp.hkv / hpw : kp.hkv;
+}
 // Many splits over few rows: the row-per-workgroup kernel, whose split lanes load in parallel;
 // otherwise one thread per 4 output elements walking the splits.
 hipError_t launch_combine(const CParams& cp, hipStream_t stream) {
   const int64_t rows = (int64_t)cp.batch * cp.max_sq * cp.hq;
-  if (cp.nsplit > 16 && rows < (1 << 20)) {
+  // many partials per row: static splits above 16, or a schedule averaging more than 16
+  // workers per sequence (cp.nsplit holds the worker count then)
+  const bool wide = cp.sched ? cp.nsplit > 16 * (int64_t)cp.batch : cp.nsplit > 16;
+  if (wide && rows < (1 << 20)) {
     const dim3 grid((unsigned)rows);
     const int cg = cp.dv / 4;
     if (cg <= 16) hipLaunchKernelGGL(fa8_combine_wide_kernel<16>, grid, dim3(1024), 0, stream, cp);

@@ -192,6 +192,60 @@ fa8_status fa8_fwd_decode_splitkv(const fa8_fwd_params* p, int32_t num_splits, f
 #define FA8_NOALLOC_SCRATCH_BYTES (32u << 20)
 fa8_status fa8_fwd_decode_noalloc(const fa8_fwd_params* p, int32_t num_splits, void* stream);
 
+/*
+ * Balanced split-KV decode for skewed sequence lengths: the split counts follow each request's
+ * length, computed on the device into a caller-owned buffer of fixed size, so every launch
+ * decision stays host-side and a graph that replays these calls sees fresh lengths each time
+ * (the static splits of fa8_fwd_decode_splitkv give a long and a short sequence the same number
+ * of splits, which leaves the waves of short sequences idle at the end; the Hopper FP8 page lists
+ * dynamic per-request splits among the features it does not include, and the FlashInfer
+ * fp8_paged_mqa_logits page describes a device-side schedule with the hazard of replaying a stale
+ * one under CUDA graphs). Two calls, in stream order:
+ *   fa8_fwd_decode_scheduled derives the schedule for num_workers workers from the device-side
+ *                            lengths, writes it into `schedule` and writes the partials, one wave
+ *                            per (kv head unit, segment) (up to 64 sequences every wave derives
+ *                            the schedule itself; beyond, one small kernel writes it first);
+ *   fa8_combine_scheduled    reads the schedule and merges each row's partials into out / lse.
+ * fa8_decode_schedule writes the same schedule on its own (to inspect it, or to size work).
+ * Partition: each sequence's visible keys (the union over its query rows, rounded out to
+ * FA8_SPLIT_GRANULE-key granules as for the static splits) are laid end to end, G granules in
+ * all; worker w of W takes granules [floor(w G / W), floor((w + 1) G / W)) of that list, so every
+ * worker has the same number of granules within one. The segments of a sequence are its workers
+ * owner(first granule) .. owner(last granule), owner(x) = floor(((x + 1) W - 1) / G) (when W > G
+ * some workers hold no granule, and such a worker between two of a sequence's workers gives it an
+ * empty segment); each is one online softmax over its keys (as one static split) and writes one
+ * partial (an empty one O = 0, LSE = -inf), at partial slot j for the j-th segment in (sequence,
+ * worker) order.
+ * Schedule layout (int32, fa8_decode_schedule_bytes(batch)): [0] G, [1] W, then the exclusive
+ * prefix of the sequences' granule counts ([batch + 1] entries), then the exclusive prefix of
+ * their segment counts ([batch + 1] entries; sequence b owns slots pst[b] .. pst[b+1]-1).
+ * Partials: o_partial [num_workers + batch, max_seqlen_q, heads_q, dv] and lse_partial
+ * [num_workers + batch, max_seqlen_q, heads_q] fp32 (fa8_decode_scheduled_workspace_bytes; at
+ * most W + batch - 1 slots are used). Limits: num_workers + batch <= FA8_MAX_WORKERS; at most 32
+ * packed rows (max_seqlen_q x heads_q / heads_kv) per kv head, else FA8_ERR_UNSUPPORTED.
+ * kernel: as for fa8_fwd_decode_splitkv_ex. The combine must read the schedule the decode wrote
+ * for the same lengths (same stream, in order); a schedule left from other lengths gives wrong
+ * merges.
+ */
+#define FA8_MAX_WORKERS 65535
+size_t fa8_decode_schedule_bytes(int32_t batch);
+size_t fa8_decode_scheduled_workspace_bytes(int32_t num_workers, int32_t batch, int32_t max_seqlen_q,
+                                            int32_t heads_q, int32_t dv);
+/* Workers for the balanced decode from host-side values only: about one wave per SIMD (4 per
+ * compute unit over the kv head units of a worker), at least four granules per worker on average
+ * when every sequence is max_seqlen_k long. cu_count <= 0 means 256. */
+int32_t fa8_decode_num_workers(const fa8_fwd_params* p, int32_t cu_count);
+fa8_status fa8_decode_schedule(const fa8_fwd_params* p, int32_t num_workers, int32_t* schedule, void* stream);
+fa8_status fa8_fwd_decode_scheduled(const fa8_fwd_params* p, int32_t num_workers, int32_t* schedule,
+                                    int32_t kernel, float* o_partial, float* lse_partial, void* stream);
+fa8_status fa8_combine_scheduled(const float* o_partial, const float* lse_partial, const int32_t* schedule,
+                                 int32_t num_workers, int32_t batch, int32_t max_seqlen_q,
+                                 const int32_t* cu_seqlens_q, int32_t heads_q, int32_t dv, void* out,
+                                 int64_t o_batch_stride, int64_t o_row_stride, int64_t o_head_stride,
+                                 int32_t out_dtype, float* lse, int64_t lse_batch_stride,
+                                 int64_t lse_head_stride, int64_t lse_row_stride, const float* sink,
+                                 void* stream);
+
 /* Decode kernels fa8_fwd_decode_splitkv_ex can be asked for (fa8_decode_plan_info.kernel).
  * AUTO is the library's choice (what fa8_fwd_decode_splitkv uses). PER_HEAD takes every problem.
  * HEAD_GROUP (several kv heads per wave, whole token rows) takes (d, dv) = (64, 64) or

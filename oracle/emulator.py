@@ -92,7 +92,7 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
 def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_splits: int = 1, sink_stage: str = "finalize",
             l_from_rounded: bool = False, heads: Optional[list] = None, batches: Optional[list] = None,
             stats: Optional[dict] = None, interleave: int = 1, granule: Optional[int] = None,
-            rows_of: Optional[dict] = None):
+            rows_of: Optional[dict] = None, split_granules: Optional[dict] = None):
     """Run the method on every query row of the selected (batch, head) pairs.
 
     Splits cut the keys into contiguous runs of granules of `granule` keys (default tile_n;
@@ -102,6 +102,10 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
     the log-sum-exp combine, like the splits themselves (the split-KV construction: parts of the
     KV range rescaled independently and merged by their LSEs, "Native FP8 (E4M3 Q/K/V) forward
     for Hopper", Design, Decode launches).
+
+    split_granules, if given, maps a batch index to its splits as a list of granule ranges
+    [(g0, g1), ...] (granules of `granule` keys counted from key 0), in place of the equal
+    shares of num_splits; the splits are merged by the combine as usual.
 
     rows_of, if given, maps a batch index to the query rows (indices into that sequence) to run;
     every row's online softmax is independent of the others, so a subset gives exactly the rows
@@ -180,9 +184,13 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
             per = g_keys // tile_n
             ngran = (sk + g_keys - 1) // g_keys
             parts_o, parts_l = [], []
-            for s, k in [(s, k) for s in range(num_splits) for k in range(interleave)]:
-                t0 = ((s * ngran) // num_splits) * per
-                t1 = min((((s + 1) * ngran) // num_splits) * per, ntiles)
+            if split_granules is not None:
+                # a sequence with no granules has one empty split (O = 0, LSE = -inf)
+                ranges = [(g0 * per, min(g1 * per, ntiles)) for g0, g1 in split_granules[b]] or [(0, 0)]
+            else:
+                ranges = [(((s * ngran) // num_splits) * per, min((((s + 1) * ngran) // num_splits) * per, ntiles))
+                          for s in range(num_splits)]
+            for (t0, t1), k in [(r, k) for r in ranges for k in range(interleave)]:
                 m = np.full(n_all, -np.inf, np.float32)
                 l = np.zeros(n_all, np.float32)
                 o = np.zeros((n_all, dv), np.float32)
@@ -231,7 +239,7 @@ def emulate(inp, tile_n: int = 64, tau: float = 0.75, bias: float = 8.0, num_spl
                 parts_o = [x[0] for x in merged]
                 parts_l = [x[1] for x in merged]
             zc = zrow if (zrow is not None and sink_stage == "combine") else None
-            if num_splits == 1 and zc is None:
+            if len(ranges) == 1 and zc is None:
                 ro, rl = parts_o[0], parts_l[0]
             else:
                 ro, rl = combine(np.stack(parts_o), np.stack(parts_l), sink=zc)

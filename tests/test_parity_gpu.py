@@ -14,7 +14,7 @@ from fa8_fwd_amd import binding
 from fa8_fwd_amd import inputs as gen
 
 from helpers import (GRANULE, LSE_ATOL, LSE_MANY_KEYS, check_against_oracle, compare, compare_lse, decode_schedule,
-                     decode_splits, prefill_tile, run_decode, run_prefill, split_key_ranges, tensors)
+                     decode_splits, milder_descales, prefill_tile, run_decode, run_prefill, split_key_ranges, tensors)
 
 pytestmark = pytest.mark.gpu
 
@@ -180,9 +180,9 @@ def _decode_check(inp, num_splits, what, kernel=binding.DECODE_AUTO):
 @pytest.mark.parametrize("kernel", [binding.DECODE_HEAD_GROUP, binding.DECODE_PER_HEAD])
 @pytest.mark.parametrize("num_splits", [1, 3, None])
 def test_decode_paged_gqa(num_splits, kernel):
-    # the paged GQA decode workload at batch 8: lengths 1k-4k, per-(b, kv_head) descales; both
-    # decode kernels (whole-row and per-head)
-    inp = gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096)
+    # the paged GQA decode workload at batch 8: lengths 1k-4k, per-(b, kv_head) descales (q, k
+    # milder: helpers.milder_descales); both decode kernels (whole-row and per-head)
+    inp = milder_descales(gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096), 81)
     _decode_check(inp, num_splits, f"paged decode b8 splits={num_splits} kernel={kernel}", kernel)
 
 
@@ -324,7 +324,8 @@ def test_prefill_sink_empty_rows():
 
 @pytest.mark.parametrize("num_splits", [1, 3, None])
 def test_decode_paged_with_sink(num_splits):
-    inp = gen.with_sink(gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096), 10, mean=4.0, std=2.0)
+    inp = gen.with_sink(milder_descales(gen.paged_gqa_decode(1, batch=8, lo=1024, hi=4096), 82), 10, mean=4.0,
+                        std=2.0)
     _decode_check(inp, num_splits, f"paged decode with sink splits={num_splits}")
 
 
