@@ -49,7 +49,7 @@ int ilog2_exact(int x) {
 constexpr int64_t kMaxLen = (int64_t)1 << 30;
 // A launch's grid may hold at most 2^32 - 1 threads along x: 2^24 workgroups of 256 threads
 // (prefill), 2^26 of 64 (decode).
-constexpr int64_t kMaxPrefillGrid = (int64_t)1 << 24;
+constexpr int64_t kMaxGridThreads = (int64_t)1 << 32;
 constexpr int64_t kMaxDecodeGridX = (int64_t)1 << 26;
 
 fa8_status check_descale(const fa8_descale& ds, const char* name) {
@@ -59,9 +59,10 @@ fa8_status check_descale(const fa8_descale& ds, const char* name) {
   return FA8_OK;
 }
 
-// Workgroups of a prefill launch (fa8::prefill_grid of the kernel parameters the launch builds).
-int64_t prefill_workgroups(const fa8_fwd_params* p) {
-  const int64_t nmb = ((int64_t)p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
+// Workgroups of a prefill launch with `rows` query rows per workgroup (fa8::prefill_grid of the
+// kernel parameters the launch builds).
+int64_t prefill_workgroups(const fa8_fwd_params* p, int rows) {
+  const int64_t nmb = ((int64_t)p->max_seqlen_q + rows - 1) / rows;
   const int64_t g = p->heads_kv > 0 ? p->heads_q / p->heads_kv : 0;
   if (p->cu_seqlens_q || p->cu_seqlens_k || p->seqused_k)
     return (int64_t)8 * (((int64_t)p->batch * p->heads_kv + 7) / 8) * nmb * g;
@@ -124,9 +125,11 @@ fa8_status validate(const fa8_fwd_params* p, int32_t num_splits) {
     for (int64_t s : so)
       if (s < 0 || s % 4 != 0) return fail(FA8_ERR_INVALID, "out strides must be non-negative multiples of 4");
     if (p->lse && !aligned(p->lse, 4)) return fail(FA8_ERR_INVALID, "lse must be 4-byte aligned");
-    if (prefill_workgroups(p) >= kMaxPrefillGrid)
-      return fail(FA8_ERR_INVALID, "prefill needs %lld workgroups of 256 threads, more than one launch can hold (2^24)",
-                  (long long)prefill_workgroups(p));
+    const int64_t wgs = prefill_workgroups(p, fa8::kPrefillRows);
+    const int nt = fa8::kPrefillThreads;
+    if (wgs * nt >= kMaxGridThreads)
+      return fail(FA8_ERR_INVALID, "prefill needs %lld workgroups of %d threads, more than one launch can hold "
+                  "(2^32 threads)", (long long)wgs, nt);
   } else {
     const int64_t rows = (int64_t)p->max_seqlen_q * (p->heads_q / p->heads_kv);
     if (rows > kMaxLen) return fail(FA8_ERR_INVALID, "too many packed decode rows");
@@ -342,11 +345,12 @@ fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream) {
   if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
   if (validate_env() && (st = validate_device_data(p, stream)) != FA8_OK) return st;
   fa8::KParams k = make_kparams(p);
-  k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
+  const int rows = fa8::kPrefillRows;
+  k.nmb = (p->max_seqlen_q + rows - 1) / rows;
   // lengths read on the device: deal the (batch, kv head) groups to the XCDs round-robin
   if (p->cu_seqlens_q || p->cu_seqlens_k || p->seqused_k)
     k.bk8 = (int32_t)(((int64_t)p->batch * p->heads_kv + 7) / 8);
-  if (fa8::prefill_grid(k) != prefill_workgroups(p)) return fail(FA8_ERR_INVALID, "internal: prefill grid mismatch");
+  if (fa8::prefill_grid(k) != prefill_workgroups(p, rows)) return fail(FA8_ERR_INVALID, "internal: prefill grid mismatch");
   hipError_t e = fa8::launch_prefill(k, p->d, p->dv, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA8_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -379,7 +383,8 @@ fa8_status fa8_fwd_prefill_mx(const fa8_fwd_params* p, const fa8_mx_scales* s, v
   if (p->batch == 0 || p->heads_q == 0 || p->max_seqlen_q == 0) return ok();
   fa8::KParams k = make_kparams(p);
   k.nmb = (p->max_seqlen_q + fa8::kPrefillRows - 1) / fa8::kPrefillRows;
-  if (fa8::prefill_grid(k) != prefill_workgroups(p)) return fail(FA8_ERR_INVALID, "internal: prefill grid mismatch");
+  if (fa8::prefill_grid(k) != prefill_workgroups(p, fa8::kPrefillRows))
+    return fail(FA8_ERR_INVALID, "internal: prefill grid mismatch");
   k.q_mx = s->q; k.qmx_bs = s->q_batch_stride; k.qmx_rs = s->q_row_stride; k.qmx_hs = s->q_head_stride;
   k.k_mx = s->k; k.kmx_bs = s->k_batch_stride; k.kmx_rs = s->k_row_stride; k.kmx_hs = s->k_head_stride;
   k.v_mx = s->v; k.vmx_bs = s->v_batch_stride; k.vmx_ts = s->v_block_stride; k.vmx_hs = s->v_head_stride;

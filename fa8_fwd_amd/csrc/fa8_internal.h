@@ -68,8 +68,10 @@ struct QParams {
 constexpr int kQuantRows = 32;
 hipError_t launch_quantize_q(const QParams& qp, hipStream_t stream);
 
-// Rows per workgroup of the prefill kernel and of the decode kernel.
+// Rows per workgroup of the prefill kernels (4 waves of 32 rows, 256 threads) and of the decode
+// kernel.
 constexpr int kPrefillRows = 128;
+constexpr int kPrefillThreads = 256;
 
 // Workgroups of a prefill launch: one per (row block, q head, batch), or, with per-sequence
 // lengths, 8 * bk8 * nmb * g (the round-robin deal of (batch, kv head) groups over the 8 XCDs

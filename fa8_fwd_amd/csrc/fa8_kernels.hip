@@ -554,14 +554,29 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
   const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
 
-  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order, its row sum on the MFMA (an all-ones
-  //      A operand, E4M3 1.0 = 0x38, makes every output row the sum over this lane's query row's
-  //      keys) and O_tile = V^T P^T from zero. At dv = 128 with two 64-key halves, each half's PV
-  //      MFMAs follow its own exponentials, so they overlap those of the next half (measured
-  //      faster there; slower at dv = 64 and 96, and at dv >= 192 the O_tile registers kept live
-  //      would spill). Otherwise O_tile goes column block by column block after all of P ----
-  constexpr bool kOverlap = PK > 1 && NB == 4;
-  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  // ---- O = alpha * O, only when some row of the wave moved its max (rare once the maxima
+  //      settle): the PV products below accumulate onto O on the matrix cores, whose accumulator
+  //      input is added at fp32 precision on gfx950 (measured: chained accumulation over 128k
+  //      keys matches a separate fp32 fold of per-tile products to within 4e-6 of sum |p v|,
+  //      with no drift), so no separate O_tile and fold are needed ----
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int n = 0; n < NB; n++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) oacc[n][r] *= alpha;
+  }
+
+  // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order, its row sum on the matrix cores and
+  //      O += V^T P^T. Each 64-key half's PV MFMAs follow its own exponentials, so they overlap
+  //      those of the next half. Row sum, dv <= 128: P as the B operand of the 16x16x128 MFMA,
+  //      whose column j collects lanes j, j+16, j+32 and j+48 (both key halves of query rows j
+  //      and j+16); a selector A operand (E4M3 1.0 = 0x38 in lane i+16q when q%2 == (i/4)%2,
+  //      else 0) makes output rows 4(L/16) .. +3 of lane L the sum over the keys of query row
+  //      L%32, the lane's own row, at half the MFMA work of a 32x32 product. dv > 128: an
+  //      all-ones A operand on the 32x32x64 MFMA (no registers to spare for the selector) ----
+  constexpr bool kRowSum16 = DV <= 128;
+  const int sel = kRowSum16 ? (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1) ? 0x38383838 : 0) : 0x38383838;
+  const v8i rsel = {sel, sel, sel, sel, sel, sel, sel, sel};
   const int trj = (lane & 15) >> 1;
   const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
   const int tr_chunk_hi = (lane >> 4) & 1;
@@ -579,10 +594,11 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
     }
     return vop;
   };
-  v8i pop[PK];
-  v16f rs, ot[kOverlap ? NB : 1];
+  v4f rs;
+  v16f rs32;
 #pragma unroll
   for (int pk = 0; pk < PK; pk++) {
+    v8i pop;
 #pragma unroll
     for (int w = 0; w < 8; w++) {
       const int kb = 2 * pk + (w >> 2), r0 = 4 * (w & 3);
@@ -592,31 +608,18 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nb));
       int word = cvt_pk_fp8_lo(p0, p1);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-      pop[pk][w] = word;
+      pop[w] = word;
     }
-    if constexpr (kOverlap) {
 #pragma unroll
-      for (int n = 0; n < NB; n++) {
-        const v8i vop = v_operand(pk, n);
-        ot[n] = (pk == 0) ? mfma_32x32x64_fp8(vop, pop[0], (v16f){}) : mfma_32x32x64_fp8(vop, pop[pk], ot[n]);
-      }
-    }
+    for (int n = 0; n < NB; n++) oacc[n] = mfma_32x32x64_fp8(v_operand(pk, n), pop, oacc[n]);
     // the row sum after the PV MFMAs of the half: its result is read last
-    rs = (pk == 0) ? mfma_32x32x64_fp8(ones, pop[0], (v16f){}) : mfma_32x32x64_fp8(ones, pop[pk], rs);
+    if constexpr (kRowSum16)
+      rs = (pk == 0) ? mfma_16x16x128_fp8(rsel, pop, (v4f){0.0f, 0.0f, 0.0f, 0.0f}) : mfma_16x16x128_fp8(rsel, pop, rs);
+    else
+      rs32 = (pk == 0) ? mfma_32x32x64_fp8(rsel, pop, (v16f){}) : mfma_32x32x64_fp8(rsel, pop, rs32);
   }
-  l_run = alpha * l_run + rs[0];
-  // ---- O = alpha * O + O_tile ----
-#pragma unroll
-  for (int n = 0; n < NB; n++) {
-    if constexpr (!kOverlap) {
-      ot[0] = mfma_32x32x64_fp8(v_operand(0, n), pop[0], (v16f){});
-#pragma unroll
-      for (int pk = 1; pk < PK; pk++) ot[0] = mfma_32x32x64_fp8(v_operand(pk, n), pop[pk], ot[0]);
-    }
-    const v16f& t = ot[kOverlap ? n : 0];
-#pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], t[r]);
-  }
+  if constexpr (kRowSum16) l_run = alpha * l_run + rs[0];
+  else l_run = alpha * l_run + rs32[0];
 }
 
 // One 64-key tile for decode, on the 16x16x128 FP8 MFMA: NQB blocks of 16 query rows (decode

@@ -146,11 +146,12 @@ typedef struct {
  * Full forward pass into p->out (and p->lse when set): one workgroup per block of query rows
  * of one query head, looping over the visible KV tiles ("Native FP8 ... for Hopper", Design;
  * the method's steps: FP8 Q K^T, scale and mask, lazy-rescaled exp2 softmax with the 2^8 P
- * bias, E4M3 P, FP8 PV accumulated per KV tile and folded into fp32 O, v descale and 1/l at
- * the end). Works for fixed, varlen and paged K/V. KV tile: 128 keys when d + dv <= 256, else
- * 64, counted from key 0 of the sequence; each tile is one step of the online softmax (row max,
- * lazy rescale, P, PV from zero, fold into O). FA8_ERR_INVALID also when the launch would need
- * 2^24 or more workgroups of 256 threads (ceil(max_seqlen_q / 128) x query heads x batch; for
+ * bias, E4M3 P, FP8 PV accumulated into fp32 O, v descale and 1/l at the end). Works for
+ * fixed, varlen and paged K/V. KV tile: 128 keys when d + dv <= 256, else 64, counted from key
+ * 0 of the sequence; each tile is one step of the online softmax (row max, lazy rescale of l
+ * and O, P, PV onto O; the matrix cores add their accumulator input at fp32 precision, so O
+ * needs no separate per-tile fold). FA8_ERR_INVALID also when the launch would need 2^32 or
+ * more threads: ceil(max_seqlen_q / 128) x query heads x batch workgroups of 256 threads (for
  * varlen or seqused_k inputs the batch x kv-head count is rounded up to a multiple of 8 first).
  */
 fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);

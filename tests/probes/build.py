@@ -4,7 +4,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PROBES = {"mfma_dot.hip": "libmfma_dot.so"}
+PROBES = {"mfma_dot.hip": "libmfma_dot.so", "mfma_acc.hip": "libmfma_acc.so"}
 
 
 def build() -> None:

@@ -248,9 +248,9 @@ def test_prefill_grid_limit():
         binding._set_out(p, torch.zeros((16, hq, d), dtype=torch.bfloat16), None, True)
         return lib.fa8_fwd_prefill(ctypes.byref(p), None)
 
-    # 8 * 64 * 4096 * 8 = 2^24 workgroups
+    # 8 * 64 * 4096 * 8 = 2^24 workgroups of 256 threads
     assert status(512 * 1024) == binding.FA8_ERR_INVALID
-    assert "2^24" in binding.last_error()
+    assert "2^32 threads" in binding.last_error()
     # the same check without launching
     q = torch.zeros((16, hq, d), dtype=torch.uint8)
     k = torch.zeros((16, hkv, d), dtype=torch.uint8)
