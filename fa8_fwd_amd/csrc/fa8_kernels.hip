@@ -1155,17 +1155,22 @@ __device__ __forceinline__ void attn_tile_mx(const FA8_LDS uint8_t* kt, const FA
     pscale[kb] = (int)xe + 127;
     nbk[kb] = (m_run == kNegInf) ? 0.0f : -(m_run + xe);
   }
-  // P of each 64-key half, its row-sum MFMA and its PV MFMAs (V block scale x P block scale).
-  // At dv = 128 the PV MFMAs of a half follow its own exponentials, so they overlap those of the
-  // next half (as in attn_tile); otherwise each column block goes after all of P.
-  constexpr bool kOverlap = PK > 1 && NB == 4;
+  // O = alpha O only when some row of the wave moved its max; the PV products then accumulate
+  // onto O on the matrix cores (their accumulator input is added at fp32 precision, as in
+  // attn_tile). P of each 64-key half, its PV MFMAs (V block scale x P block scale) right after
+  // its exponentials, so they overlap those of the next half, and its row-sum MFMA.
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+    for (int n = 0; n < NB; n++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) oacc[n][r] *= alpha;
+  }
   const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
   const FA8_LDS uint8_t* vsc_lane = vsc + hgrp * DV + lrow;        // block hgrp, column lrow
-  v8i pop[PK];
-  int psc[PK];
-  v16f rs, ot[kOverlap ? NB : 1];
+  v16f rs;
 #pragma unroll
   for (int pk = 0; pk < PK; pk++) {
+    v8i pop;
 #pragma unroll
     for (int w = 0; w < 8; w++) {
       const int kb = 2 * pk + (w >> 2), r0 = 4 * (w & 3);
@@ -1175,41 +1180,19 @@ __device__ __forceinline__ void attn_tile_mx(const FA8_LDS uint8_t* kt, const FA
       const float p3 = fast_exp2(__builtin_fmaf(sacc[kb][r0 + 3], c, nbk[kb]));
       int word = cvt_pk_fp8_lo(p0, p1);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, word, true);
-      pop[pk][w] = word;
+      pop[w] = word;
     }
-    psc[pk] = hgrp ? pscale[2 * pk + 1] : pscale[2 * pk];   // this lane half's key block
-    if constexpr (kOverlap) {
+    const int psc = hgrp ? pscale[2 * pk + 1] : pscale[2 * pk];   // this lane half's key block
 #pragma unroll
-      for (int n = 0; n < NB; n++) {
-        __builtin_amdgcn_sched_barrier(0);   // one V operand read ahead at a time
-        const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
-        ot[n] = (pk == 0) ? mfma_32x32x64_mx(pv_operand_mx<DV>(vt, 0, n, lane), pop[0], (v16f){}, sa, psc[0])
-                          : mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop[pk], ot[n], sa, psc[pk]);
-      }
+    for (int n = 0; n < NB; n++) {
+      __builtin_amdgcn_sched_barrier(0);   // one V operand read ahead at a time
+      const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
+      oacc[n] = mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop, oacc[n], sa, psc);
     }
     // row sum of the stored P times its scales
-    rs = (pk == 0) ? mfma_32x32x64_mx(ones, pop[0], (v16f){}, 127, psc[0])
-                   : mfma_32x32x64_mx(ones, pop[pk], rs, 127, psc[pk]);
+    rs = (pk == 0) ? mfma_32x32x64_mx(ones, pop, (v16f){}, 127, psc) : mfma_32x32x64_mx(ones, pop, rs, 127, psc);
   }
   l_run = alpha * l_run + rs[0];
-
-  // ---- O = alpha O + O_tile ----
-  if constexpr (!kOverlap) __builtin_amdgcn_sched_barrier(0);   // keeps the V reads out of the exponentials
-#pragma unroll
-  for (int n = 0; n < NB; n++) {
-    if constexpr (!kOverlap) {
-#pragma unroll
-      for (int pk = 0; pk < PK; pk++) {
-        const int sa = (int)vsc_lane[2 * pk * DV + 32 * n];
-        ot[0] = (pk == 0) ? mfma_32x32x64_mx(pv_operand_mx<DV>(vt, 0, n, lane), pop[0], (v16f){}, sa, psc[0])
-                          : mfma_32x32x64_mx(pv_operand_mx<DV>(vt, pk, n, lane), pop[pk], ot[0], sa, psc[pk]);
-      }
-    }
-    const v16f& t = ot[kOverlap ? n : 0];
-#pragma unroll
-    for (int r = 0; r < 16; r++) oacc[n][r] = __builtin_fmaf(alpha, oacc[n][r], t[r]);
-    if constexpr (!kOverlap) __builtin_amdgcn_sched_barrier(0);
-  }
 }
 
 // 4 waves x 32 query rows of one query head; K/V tiles by direct global->LDS copies (two

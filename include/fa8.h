@@ -329,8 +329,8 @@ fa8_status fa8_quantize_q(const fa8_quant_params* p, void* workspace, void* stre
  * softmax keeps the
  * lazy rescale of fa8_fwd_prefill (the running max moves only when a tile's max exceeds it by
  * more than 0.75); there is no 2^8 offset (the block scales cover the range). The row sum is
- * taken over the stored P times its scales, and each tile's PV is accumulated from zero and
- * folded into fp32 O as in fa8_fwd_prefill.
+ * taken over the stored P times its scales, and each tile's PV is accumulated onto fp32 O on
+ * the matrix cores as in fa8_fwd_prefill.
  *
  * p: as for fa8_fwd_prefill with these limits: (d, dv) = (64, 64) or (128, 128); fixed-length
  *   Q and K/V (cu_seqlens_q, cu_seqlens_k, seqused_k and block_table NULL); the descales of p
