@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, launched as the benchmark launches them (the
-library's own split heuristic), against the fp64 CPU oracle on rows it computes one by one:
+library's own split heuristic, and the balanced decode at the library's worker count), against the fp64 CPU oracle on rows it computes one by one:
 every row where that is cheap (decode), else a seeded sample that includes the first and last
 rows, row-block and tile boundaries and the ragged tails. The rule is the one of every GPU test
 (helpers.check_rows), with the method emulator run on the same rows. Also the long-KV accuracy
@@ -12,8 +12,8 @@ import oracle
 from fa8_fwd_amd import binding
 from fa8_fwd_amd import inputs as gen
 
-from helpers import (GRANULE, check_rows, decode_schedule, decode_splits, emulate_mx_rows, emulate_rows, gather,
-                     prefill_tile, run_decode, run_prefill)
+from helpers import (GRANULE, balanced_schedule, check_rows, decode_schedule, decode_splits, emulate_mx_rows,
+                     emulate_rows, gather, prefill_tile, run_decode, run_decode_balanced, run_prefill, tensors)
 from test_mx_gpu import run_mx
 
 pytestmark = pytest.mark.gpu
@@ -71,6 +71,36 @@ def test_paged_gqa_decode_max_seqlen_32k():
     # the same sequences launched with max_seqlen_k = 32768 and a block table that wide, as the
     # Hopper FP8 page's decode measurements set up the launch (Performance setup)
     _decode_rows(gen.paged_gqa_decode(1, max_seqlen_k=32768), "paged GQA decode b64, max_seqlen_k 32768")
+
+
+def _decode_balanced_rows(inp, what):
+    # the balanced decode at the worker count the library picks (fa8_decode_num_workers), the
+    # launch the benchmark times for the decode step
+    q, k, v, kw = tensors(inp)
+    W = binding.decode_num_workers(q, k, v, **kw)
+    del q, k, v, kw
+    got, glse = run_decode_balanced(inp, W)
+    rows = oracle.all_rows(inp)
+    o, l = gather(inp, got, glse, rows)
+    _, _, _, segs = balanced_schedule(inp, W)
+    bk, kg = decode_schedule(inp, 1)
+    emu_d = emulate_rows(inp, rows, tile_n=GRANULE, split_granules=segs, sink_stage="combine")
+    emu_s = emulate_rows(inp, rows, tile_n=bk, interleave=kg, granule=GRANULE, split_granules=segs,
+                         sink_stage="combine")
+    ref = oracle.attention(inp, rows=rows)
+    print(check_rows(inp, rows, o, l, f"{what} W={W}", emu_d, emu_s, ref=ref), flush=True)
+    return o, ref[0]
+
+
+def test_paged_gqa_decode_balanced_full_size_every_row():
+    _decode_balanced_rows(gen.paged_gqa_decode(1), "balanced paged GQA decode b64 (every row)")
+
+
+def test_long_kv_decode_balanced_full_size_every_row():
+    o, ref = _decode_balanced_rows(gen.long_kv_decode(3), "balanced long-KV decode b4 k131072 (every row)")
+    ratio = float(o.mean() / ref.mean())
+    print(f"balanced long-KV output mean ratio gpu/oracle {ratio:.5f}", flush=True)
+    assert 0.99 <= ratio <= 1.01
 
 
 def test_causal_prefill_full_size_sampled_rows():
