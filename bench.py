@@ -526,7 +526,7 @@ def main():
         line["prefill"] = {
             "workload": pre.name, "value": round(tfl, 2), "unit": "TFLOP/s", "ms_per_step": round(p_ms, 4),
             "steps": args.prefill_steps, "flop_per_step": flop, "pct_of_fp8_peak": round(100 * tfl / FP8_PEAK_TFLOPS, 2),
-            "roofline": {"bound": "mfma", "kernel": "fa8_prefill_kernel<128,128,128,false> (prefill, contiguous K/V)",
+            "roofline": {"bound": "mfma", "kernel": "fa8_prefill_kernel<128,128,64,false> (prefill, contiguous K/V, 64-key tiles)",
                          "achieved": round(ktfl, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ktfl / FP8_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic(f"fa8_prefill_kernel_{pre.name}_traffic.md"),

@@ -488,22 +488,14 @@ __device__ __forceinline__ v8i pv_operand_mx(const FA8_LDS uint8_t* vt, int pk, 
   return vop;
 }
 
-// One KV tile of BN keys (LDS K tile at kt, V tile at vt, both row-major and swizzled) for the
-// 32 query rows of this wave. Updates the running max m, row sum l and O accumulators.
-template <int D, int DV, int BN>
-__device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_LDS uint8_t* vt,
-                                          const v8i (&qop)[(D + 63) / 64], float c, bool need_mask, int j0,
-                                          int my_lo, int my_hi, int lane, float& m_run, float& l_run,
-                                          v16f (&oacc)[DV / 32]) {
+// S^T = K Q^T of one tile of BN keys (the first part of attn_tile).
+template <int D, int BN>
+__device__ __forceinline__ void qk_tile(const FA8_LDS uint8_t* kt, const v8i (&qop)[(D + 63) / 64], int lane,
+                                        v16f (&sacc)[BN / 32]) {
   constexpr int KB = BN / 32;        // 32-key blocks of S^T
-  constexpr int PK = BN / 64;        // 64-key k-steps of PV
   constexpr int KS = (D + 63) / 64;  // k-steps of QK
-  constexpr int NB = DV / 32;
-  constexpr int KCH = D / 16, VCH = DV / 16;
+  constexpr int KCH = D / 16;
   const int hgrp = lane >> 5, lrow = lane & 31;
-
-  // ---- S^T = K Q^T ----
-  v16f sacc[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; kb++) {
 #pragma unroll
@@ -522,6 +514,19 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
       sacc[kb] = mfma_32x32x64_fp8(kop, qop[ks], sacc[kb]);
     }
   }
+}
+
+// The rest of a tile given its S^T: mask, row max, lazy rescale of l and O, P, PV onto O and
+// the row sum (the second part of attn_tile).
+template <int D, int DV, int BN>
+__device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, v16f (&sacc)[BN / 32], float c,
+                                                bool need_mask, int j0, int my_lo, int my_hi, int lane,
+                                                float& m_run, float& l_run, v16f (&oacc)[DV / 32]) {
+  constexpr int KB = BN / 32;        // 32-key blocks of S^T
+  constexpr int PK = BN / 64;        // 64-key k-steps of PV
+  constexpr int NB = DV / 32;
+  constexpr int VCH = DV / 16;
+  const int hgrp = lane >> 5;
 
   // ---- mask (only tiles that cross some row's key bounds): key j is visible iff
   //      my_lo <= j < my_hi, one unsigned compare (an empty row has span 0) ----
@@ -620,6 +625,18 @@ __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_L
   }
   if constexpr (kRowSum16) l_run = alpha * l_run + rs[0];
   else l_run = alpha * l_run + rs32[0];
+}
+
+// One KV tile of BN keys (LDS K tile at kt, V tile at vt, both row-major and swizzled) for the
+// 32 query rows of this wave. Updates the running max m, row sum l and O accumulators.
+template <int D, int DV, int BN>
+__device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_LDS uint8_t* vt,
+                                          const v8i (&qop)[(D + 63) / 64], float c, bool need_mask, int j0,
+                                          int my_lo, int my_hi, int lane, float& m_run, float& l_run,
+                                          v16f (&oacc)[DV / 32]) {
+  v16f sacc[BN / 32];
+  qk_tile<D, BN>(kt, qop, lane, sacc);
+  softmax_pv_tile<D, DV, BN>(vt, sacc, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
 }
 
 // One 64-key tile for decode, on the 16x16x128 FP8 MFMA: NQB blocks of 16 query rows (decode
@@ -2315,9 +2332,12 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
   }
 }
 
-// KV tile of the prefill kernel: 128 keys when a two-stage tile pair fits twice in LDS, else 64.
+// KV tile of the prefill kernel: 64 keys when d + dv > 256 (a two-stage pair of 128-key tiles
+// would not fit twice in LDS) and at (128, 128), where it leaves 152 VGPRs and so three waves per
+// SIMD instead of two (measured 4.5% faster on the causal prefill; slower at d = 64, where 128-key
+// tiles already run three); else 128.
 template <int D, int DV>
-constexpr int prefill_tile() { return (D + DV) <= 256 ? 128 : 64; }
+constexpr int prefill_tile() { return (D == 128 && DV == 128) || (D + DV) > 256 ? 64 : 128; }
 
 template <int D, int DV>
 static hipError_t launch_prefill_t(const KParams& kp, hipStream_t stream) {

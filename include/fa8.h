@@ -147,8 +147,8 @@ typedef struct {
  * of one query head, looping over the visible KV tiles ("Native FP8 ... for Hopper", Design;
  * the method's steps: FP8 Q K^T, scale and mask, lazy-rescaled exp2 softmax with the 2^8 P
  * bias, E4M3 P, FP8 PV accumulated into fp32 O, v descale and 1/l at the end). Works for
- * fixed, varlen and paged K/V. KV tile: 128 keys when d + dv <= 256, else 64, counted from key
- * 0 of the sequence; each tile is one step of the online softmax (row max, lazy rescale of l
+ * fixed, varlen and paged K/V. KV tile: 64 keys at (d, dv) = (128, 128) and when d + dv > 256,
+ * else 128, counted from key 0 of the sequence; each tile is one step of the online softmax (row max, lazy rescale of l
  * and O, P, PV onto O; the matrix cores add their accumulator input at fp32 precision, so O
  * needs no separate per-tile fold). FA8_ERR_INVALID also when the launch would need 2^32 or
  * more threads: ceil(max_seqlen_q / 128) x query heads x batch workgroups of 256 threads (for

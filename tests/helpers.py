@@ -209,9 +209,9 @@ def split_key_ranges(inp, num_splits: int):
 
 
 def prefill_tile(d: int, dv: int) -> int:
-    """KV tile of fa8_fwd_prefill as include/fa8.h states it: 128 keys when d + dv <= 256, else
-    64 (one online-softmax step per tile)."""
-    return 128 if d + dv <= 256 else 64
+    """KV tile of fa8_fwd_prefill as include/fa8.h states it: 64 keys at (d, dv) = (128, 128) and
+    when d + dv > 256, else 128 (one online-softmax step per tile)."""
+    return 64 if (d, dv) == (128, 128) or d + dv > 256 else 128
 
 
 # ---------------------------------------------------------------------------------------------
