@@ -937,6 +937,14 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     my_lo = rr.lo(qi);
     my_hi = rr.hi(qi);
   }
+  // keys any row of this wave sees: a tile outside them would add exact zeros (P = 0, no
+  // rescale), so the wave skips its math (it still copies its share and meets the barriers)
+  const int w_first = rb0 + wave * 32, w_last = min(w_first + 31, rb1);
+  int wv_lo = 0, wv_hi = 0;
+  if (w_first <= rb1) {
+    wv_lo = rr.lo(w_first);
+    wv_hi = rr.hi(w_last);
+  }
 
   const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
   const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
@@ -1024,7 +1032,8 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem + st * STAGE;
     const int j0 = t * BN;
     const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
-    attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+    if (j0 < wv_hi && j0 + BN > wv_lo)
+      attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
     wait_vmcnt<0>();   // this wave's loads of tile t+1 have landed in LDS
     __syncthreads();   // ... and every other wave's; all reads of stage st are done
   }
