@@ -778,16 +778,16 @@ __device__ __forceinline__ RowScale row_scale(const KParams& p, bool with_sink, 
 // (`stage`: 32 rows x DV halves, its own region; every 16-byte chunk c of row r at chunk
 // c ^ (r mod DV/8), which spreads both the writes and the row reads over the banks) and writes
 // whole rows with 16-byte lanes. Rows past row_last are staged but not stored.
-template <int DV>
-__device__ __forceinline__ void store_rows_staged(const KParams& p, const v16f (&oacc)[DV / 32], float inv, int lane,
-                                                  int b, int q0, int row0, int row_last, int qh,
-                                                  FA8_LDS uint8_t* stage) {
+template <int DV, bool FP16>
+__device__ __forceinline__ void store_rows_staged_t(const KParams& p, const v16f (&oacc)[DV / 32], float inv, int lane,
+                                                    int b, int q0, int row0, int row_last, int qh,
+                                                    FA8_LDS uint8_t* stage) {
   constexpr int NB = DV / 32;
   constexpr int CPR = DV / 8;     // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;   // rows per store instruction
+  constexpr int NI = 32 / RPI;    // store instructions per wave
   static_assert(CPR * RPI == 64 && (CPR & (CPR - 1)) == 0, "rows must split into 16-byte lanes");
   const int hgrp = lane >> 5, lrow = lane & 31;
-  const bool fp16 = p.out_fp16 != 0;
   // lane (row lrow, half hgrp) holds columns 32n + 8q4 + 4hgrp .. +3: half hgrp of chunk 4n + q4
 #pragma unroll
   for (int n = 0; n < NB; n++)
@@ -796,23 +796,36 @@ __device__ __forceinline__ void store_rows_staged(const KParams& p, const v16f (
       const int c = 4 * n + q4;
       const int pos = lrow * (2 * DV) + ((c ^ (lrow & (CPR - 1))) << 4) + 8 * hgrp;
       *(FA8_LDS v2i*)(stage + pos) = pack4_half(oacc[n][4 * q4] * inv, oacc[n][4 * q4 + 1] * inv,
-                                                oacc[n][4 * q4 + 2] * inv, oacc[n][4 * q4 + 3] * inv, fp16);
+                                                oacc[n][4 * q4 + 2] * inv, oacc[n][4 * q4 + 3] * inv, FP16);
     }
   // the reads below take chunks other lanes of this wave wrote: the wave's LDS operations are
   // performed in order, and the fence keeps the compiler from moving a read above a write
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   const int rr = lane / CPR, c = lane % CPR;
+  // every read first (all 32 staged rows are in bounds), then the stores of the rows that exist
+  v4i x[NI];
 #pragma unroll
-  for (int i = 0; i < 32 / RPI; i++) {
+  for (int i = 0; i < NI; i++) {
     const int r = RPI * i + rr;
-    const v4i x = *(const FA8_LDS v4i*)(stage + r * (2 * DV) + ((c ^ (r & (CPR - 1))) << 4));
-    const int qi = row0 + r;
+    x[i] = *(const FA8_LDS v4i*)(stage + r * (2 * DV) + ((c ^ (r & (CPR - 1))) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < NI; i++) {
+    const int qi = row0 + RPI * i + rr;
     if (qi <= row_last) {
       const int64_t off = (p.cu_q ? (int64_t)(q0 + qi) * p.o_rs : (int64_t)b * p.o_bs + (int64_t)qi * p.o_rs) +
                           (int64_t)qh * p.o_hs + 8 * c;
-      *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(p.out) + off) = x;
+      *reinterpret_cast<v4i*>(reinterpret_cast<uint16_t*>(p.out) + off) = x[i];
     }
   }
+}
+template <int DV>
+__device__ __forceinline__ void store_rows_staged(const KParams& p, const v16f (&oacc)[DV / 32], float inv, int lane,
+                                                  int b, int q0, int row0, int row_last, int qh,
+                                                  FA8_LDS uint8_t* stage) {
+  // the output type is chosen once, outside the conversion and store loops
+  if (p.out_fp16) store_rows_staged_t<DV, true>(p, oacc, inv, lane, b, q0, row0, row_last, qh, stage);
+  else store_rows_staged_t<DV, false>(p, oacc, inv, lane, b, q0, row0, row_last, qh, stage);
 }
 
 template <int DV, bool SPLIT>
@@ -865,7 +878,12 @@ __device__ __forceinline__ void store_row(const KParams& p, const v16f (&oacc)[D
 // of very different lengths to single XCDs, so there (p.bk8 > 0) the (batch, kv head) groups
 // are dealt to the XCDs round-robin instead, row block by row block, the deal rotating by
 // one XCD every kRankChunk row blocks: every XCD sees every sequence, and the row blocks of
-// one group that lie close together (and share K/V) still meet in one L2.
+// one group that lie close together (and share K/V) still meet in one L2. Rank r there is each
+// sequence's own r-th row block counted from its last one (causal) or first one, so the ranks
+// that only some sequences have come last. Within one rank the groups' order rotates by one
+// group per rank: an XCD hands its workgroups to its shader engines in a fixed rotation by
+// dispatch position and dispatches in order, so a sequence that kept its position from rank to
+// rank would keep its shader engines, fill them while the others idle, and stall the dispatch.
 // ------------------------------------------------------------------------------------------
 constexpr int kRankChunk = 8;
 
@@ -887,11 +905,13 @@ __device__ __forceinline__ PrefillWork prefill_work(const KParams& p) {
     wk.mbi = t1 % p.nmb;
     wk.bk = t1 / p.nmb;
   } else {
-    // grid = 8 * bk8 * nmb * g; XCD x takes at rank r the groups bk = ((x - r/kRankChunk) mod 8) + 8 i
+    // grid = 8 * bk8 * nmb * g; XCD x takes at rank r the groups bk = ((x - r/kRankChunk) mod 8) + 8 i,
+    // i = (j + r) mod bk8 at the rank's j-th position
     wk.hg = slot % g;
     const int t1 = slot / g;
     wk.mbi = t1 / p.bk8;
-    wk.bk = ((xcd - wk.mbi / kRankChunk) & 7) + 8 * (t1 % p.bk8);   // >= batch * hkv: no work
+    const int i = (t1 % p.bk8 + wk.mbi % p.bk8) % p.bk8;
+    wk.bk = ((xcd - wk.mbi / kRankChunk) & 7) + 8 * i;   // >= batch * hkv: no work
   }
   return wk;
 }
@@ -916,12 +936,15 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
   if (wk.bk >= p.batch * p.hkv) return;   // uniform: a slot of the round-robin deal with no group
   const int hg = wk.hg, mbi = wk.mbi;
   const int kvh = wk.bk % p.hkv, b = wk.bk / p.hkv;
-  const int mblock = p.causal ? p.nmb - 1 - mbi : mbi;   // causal: heaviest row blocks first
   const int qh = kvh * g + hg;
 
   const SeqInfo si = seq_info(p, b);
+  // causal: heaviest row blocks first; with per-sequence lengths the ranks count from each
+  // sequence's own last row block
+  const int nmb_b = p.bk8 ? (si.sq + BM - 1) / BM : p.nmb;
+  const int mblock = p.causal ? nmb_b - 1 - mbi : mbi;
   const int rb0 = mblock * BM;
-  if (rb0 >= si.sq) return;  // uniform: no valid row in this block
+  if (mblock < 0 || rb0 >= si.sq) return;  // uniform: no valid row in this block
   const int rb1 = min(rb0 + BM, si.sq) - 1;
   const RowRange rr{si.sk, si.sk - si.sq, p.wl, p.wr};
   int wg_lo = rr.lo(rb0), wg_hi = rr.hi(rb1);
