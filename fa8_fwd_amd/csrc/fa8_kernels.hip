@@ -1788,7 +1788,11 @@ __device__ __forceinline__ void heads_segment(const KParams& p, int b, int kvh0,
   const int qh = kvh * g + qg;
   const float dq = load_descale(p.dq, p.dq_sb, p.dq_sh, b, kvh);
   const float dk = load_descale(p.dk, p.dk_sb, p.dk_sh, b, kvh);
-  const float dvs = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh);
+  // the v descale of each head slot, wave-uniform (scalar registers): the lane's own one is
+  // picked after the key loop, so it holds no vector register through the loop
+  float dvs_slot[HPW];
+#pragma unroll
+  for (int a = 0; a < HPW; a++) dvs_slot[a] = load_descale(p.dv, p.dv_sb, p.dv_sh, b, kvh0 + a);
   const float c = p.scale_log2 * dq * dk;
   int my_lo = 0, my_hi = 0;
   if (valid) {
@@ -2077,6 +2081,10 @@ __device__ __forceinline__ void heads_segment(const KParams& p, int b, int kvh0,
   float l_tot = sum_xor16(l_run);
   l_tot = sum_xor32(l_tot);
   if (!valid) return;
+  float dvs = dvs_slot[0];
+#pragma unroll
+  for (int a = 1; a < HPW; a++)
+    if (my_a == a) dvs = dvs_slot[a];
   const bool nonempty = l_tot > 0.0f;
   const float inv = nonempty ? dvs / l_tot : 0.0f;
   const float lse = nonempty ? (m_run + __log2f(l_tot) - kBias) * kLn2 : kNegInf;
