@@ -47,6 +47,37 @@ def test_quantizer_bit_exact_varlen_with_zero_and_empty_blocks():
     assert s.cpu().numpy()[1].tolist() == [1.0, 1.0] and s.cpu().numpy()[2, 1] == 1.0
 
 
+def test_quantizer_bit_exact_across_the_scale_range():
+    # bf16 blocks whose maxima put s = amax / 448 exactly at 2^-96 (the smallest s of the
+    # kernel's short quotient path), one bf16 step below it, among the subnormals, and up to the
+    # top of the bf16 range; elements of +-0 and subnormal values inside normal blocks
+    thr = 1.75 * 2.0 ** -88                      # 448 * 2^-96, a bf16 value
+    below = (1.75 - 2.0 ** -7) * 2.0 ** -88      # the bf16 value just below it
+    amaxes = [thr, below, 2.0 ** -126, 2.0 ** -130, 1e-30, 1e-26, 1e-3, 1.0, 448.0, 3.0e5, 1e30, 3.0e38,
+              thr * 2, below / 2, 5.0e-39, 65504.0]
+    g = torch.Generator().manual_seed(7)
+    q = torch.empty((2, 40, 8, 64))
+    for blk, a in enumerate(amaxes):
+        b, kvh = divmod(blk, 8)
+        x = (torch.rand((40, 64), generator=g) * 2 - 1) * a
+        x[0, 0] = a if blk % 2 == 0 else -a     # the block maximum, either sign
+        x[1, 0:4] = torch.tensor([0.0, -0.0, 2.0 ** -133, -(2.0 ** -140)])
+        q[b, :, kvh, :] = x
+    q = q.to(torch.bfloat16)
+    assert torch.isfinite(q.float()).all()
+    dev = torch.device("cuda:0")
+    got, s = binding.quantize_q(q.to(dev), 8)
+    torch.cuda.synchronize()
+    ref, rs = quant.quantize_q(q.float().numpy(), 8)
+    # the test's scales: both quotient paths are exercised
+    sref = rs.reshape(-1)
+    assert (sref >= np.float32(2.0 ** -96)).any() and (sref < np.float32(2.0 ** -96)).any()
+    assert np.float32(2.0 ** -96) in sref
+    diff = got.cpu().numpy() != ref
+    assert not diff.any(), f"{int(diff.sum())} codes differ, first at {np.argwhere(diff)[:3].tolist()}"
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
 def test_quantized_q_through_prefill():
     # bf16 Q quantized on the GPU, then the FP8 prefill with the produced per-(b, kv head) descale,
     # against the oracle on the same codes and descales
