@@ -85,27 +85,53 @@ __global__ void __launch_bounds__(256) fa8_quant_amax_kernel(const QParams p) {
   const int vpr = p.g * (p.d / 8);                 // 8-element vectors per row of the block
   const int nv = ch.rows * vpr;
   const bool fp16 = p.in_fp16 != 0;
+  const int nt = (int)blockDim.x;
   float m = 0.0f;
   // four vectors per thread and pass, their loads issued together
   constexpr int U = 4;
-  for (int v0 = threadIdx.x; v0 < nv; v0 += U * blockDim.x) {
-    float x[U][8];
+  if (nt % vpr == 0) {
+    // whole rows per pass: a thread keeps its head and column (no divisions in the loop)
+    const int row0 = (int)threadIdx.x / vpr, rem = (int)threadIdx.x - row0 * vpr;
+    const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
+    const int step = nt / vpr;
+    const int64_t base = ch.in_row0 + (int64_t)h * p.q_hs + col;
+    for (int r0 = row0; r0 < ch.rows; r0 += U * step) {
+      float x[U][8];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int v = v0 + u * blockDim.x;
-      if (v < nv) {
-        const int r = v / vpr, rem = v - r * vpr;
-        const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
-        load8(p.q, ch.in_row0 + (int64_t)r * p.q_rs + (int64_t)h * p.q_hs + col, fp16, x[u]);
-      } else {
+      for (int u = 0; u < U; u++) {
+        const int r = r0 + u * step;
+        if (r < ch.rows) {
+          load8(p.q, base + (int64_t)r * p.q_rs, fp16, x[u]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; i++) x[u][i] = 0.0f;
+          for (int i = 0; i < 8; i++) x[u][i] = 0.0f;
+        }
       }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x[u][i]));
     }
+  } else {
+    for (int v0 = threadIdx.x; v0 < nv; v0 += U * nt) {
+      float x[U][8];
 #pragma unroll
-    for (int u = 0; u < U; u++)
+      for (int u = 0; u < U; u++) {
+        const int v = v0 + u * nt;
+        if (v < nv) {
+          const int r = v / vpr, rem = v - r * vpr;
+          const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
+          load8(p.q, ch.in_row0 + (int64_t)r * p.q_rs + (int64_t)h * p.q_hs + col, fp16, x[u]);
+        } else {
 #pragma unroll
-      for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x[u][i]));
+          for (int i = 0; i < 8; i++) x[u][i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x[u][i]));
+    }
   }
   m = block_max(m, red);
   if (threadIdx.x == 0) p.ws[((int64_t)b * p.hkv + kvh) * p.nchunk + c] = m;
@@ -123,6 +149,25 @@ __device__ __forceinline__ float quotient(float x, float s, float r) {
   }
 }
 
+// Codes of the 8 elements at (row, h, col) of the chunk
+template <bool FAST>
+__device__ __forceinline__ void apply_vec(const QParams& p, const Chunk& ch, float s, float r, bool fp16, int row,
+                                          int h, int col) {
+  float x[8];
+  load8(p.q, ch.in_row0 + (int64_t)row * p.q_rs + (int64_t)h * p.q_hs + col, fp16, x);
+  int w[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) y[i] = fminf(fmaxf(quotient<FAST>(x[4 * k + i], s, r), -kE4M3Max), kE4M3Max);
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+  }
+  uint8_t* dst = reinterpret_cast<uint8_t*>(p.q_out) + ch.out_row0 + (int64_t)row * p.o_rs + (int64_t)h * p.o_hs + col;
+  *reinterpret_cast<v2i*>(dst) = (v2i){w[0], w[1]};
+}
+
 // E4M3 codes of one chunk, every element divided by the block's s
 template <bool FAST>
 __device__ __forceinline__ void apply_chunk(const QParams& p, const Chunk& ch, float s) {
@@ -130,23 +175,22 @@ __device__ __forceinline__ void apply_chunk(const QParams& p, const Chunk& ch, f
   const int vpr = p.g * (p.d / 8);
   const int nv = ch.rows * vpr;
   const bool fp16 = p.in_fp16 != 0;
-#pragma unroll 4
-  for (int v = threadIdx.x; v < nv; v += blockDim.x) {
-    const int row = v / vpr, rem = v - row * vpr;
+  const int nt = (int)blockDim.x;
+  if (nt % vpr == 0) {
+    // the workgroup covers whole rows per pass: a thread keeps its head and column, and steps
+    // nt / vpr rows at a time (no divisions in the loop)
+    const int row0 = (int)threadIdx.x / vpr, rem = (int)threadIdx.x - row0 * vpr;
     const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
-    float x[8];
-    load8(p.q, ch.in_row0 + (int64_t)row * p.q_rs + (int64_t)h * p.q_hs + col, fp16, x);
-    int w[2];
-#pragma unroll
-    for (int k = 0; k < 2; k++) {
-      float y[4];
-#pragma unroll
-      for (int i = 0; i < 4; i++) y[i] = fminf(fmaxf(quotient<FAST>(x[4 * k + i], s, r), -kE4M3Max), kE4M3Max);
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-      w[k] = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+    const int step = nt / vpr;
+#pragma unroll 4
+    for (int row = row0; row < ch.rows; row += step) apply_vec<FAST>(p, ch, s, r, fp16, row, h, col);
+  } else {
+#pragma unroll 4
+    for (int v = threadIdx.x; v < nv; v += nt) {
+      const int row = v / vpr, rem = v - row * vpr;
+      const int h = rem / (p.d / 8), col = (rem - h * (p.d / 8)) * 8;
+      apply_vec<FAST>(p, ch, s, r, fp16, row, h, col);
     }
-    uint8_t* dst = reinterpret_cast<uint8_t*>(p.q_out) + ch.out_row0 + (int64_t)row * p.o_rs + (int64_t)h * p.o_hs + col;
-    *reinterpret_cast<v2i*>(dst) = (v2i){w[0], w[1]};
   }
 }
 
