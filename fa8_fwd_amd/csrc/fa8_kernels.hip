@@ -1433,12 +1433,20 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_mx_kernel(const KParams p)
 // no branches around its loads, so the compiler's in-order vector-memory wait counts stay
 // exact. Contiguous K/V is PAGEMODE 0.
 // ------------------------------------------------------------------------------------------
-// Tiles a decode wave keeps in flight in registers (one wave per SIMD, so the whole 512-entry
-// register file is available: DEPTH x (d + dv) / 4 registers of staging).
-// Two stages measured faster than three or four on the paged GQA decode workload (the extra
-// requests in flight only lengthen the memory queues).
+// Waves per SIMD of the per-head decode kernel, and the tiles each keeps in flight in registers
+// (DEPTH x (d + dv) / 4 registers of staging). d + dv <= 256 with one 16-row block per wave: two
+// waves per SIMD with one stage each (about 200 registers); on the long-KV decode workload
+// (131072 keys, 8 q heads per kv head) that measured 6% faster than one wave with two stages.
+// Otherwise one wave per SIMD with the whole 512-entry register file: two stages (faster than
+// three or four when this kernel carried the paged GQA decode workload; the extra requests in
+// flight only lengthen the memory queues), one where two would spill.
+template <int D, int DV, int NQB>
+constexpr int decode_waves() {
+  return (D + DV <= 256 && NQB == 1) ? 2 : 1;
+}
 template <int D, int DV, int NQB>
 constexpr int decode_depth() {
+  if (decode_waves<D, DV, NQB>() == 2) return 1;
   if (D + DV <= 256) return 2;
   if (D + DV >= 512 || NQB == 2) return 1;   // two stages would spill
   return 2;
@@ -1705,7 +1713,8 @@ __device__ __forceinline__ void perhead_segment(const KParams& p, int b, int kvh
 // One wave per (kv head, row block, split, batch) with static splits, or per (kv head, segment) of
 // a balanced schedule (SCHED; one row block per kv head).
 template <int D, int DV, int NQB, int PAGEMODE, bool SCHED>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(decode_waves<D, DV, NQB>(), decode_waves<D, DV, NQB>())))
 fa8_decode_kernel(const KParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kKvTile * (D + DV)];
   if constexpr (SCHED) {
