@@ -88,16 +88,19 @@ def test_prefill_varlen_window_fp16():
     _prefill_check(inp, "varlen d192/128 window128 fp16")
 
 
-def test_prefill_varlen_many_sequences_every_row():
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_varlen_many_sequences_every_row(causal):
     # 11 sequences x 3 kv heads = 33 (batch, kv head) groups, dealt to the 8 XCDs round-robin
     # (slots with no group exist), and up to 11 row blocks per sequence (the deal rotates every
-    # 8): every row of every head is checked, so a lost or doubled work item shows
+    # 8; ranks count from each sequence's own last row block when causal, its first otherwise,
+    # and the groups' order rotates within each rank): every row of every head is checked, so a
+    # lost or doubled work item shows
     rng = np.random.default_rng(12)
     sq = rng.integers(1, 1300, 11)
     sq[3] = 1400
     sk = sq + 256 + rng.integers(0, 200, 11)    # every row sees at least 257 keys
-    inp = gen.make_varlen(12, sq, sk, 6, 3, 64, 64, causal=True)
-    _prefill_check(inp, "varlen 11 seqs, 3 kv heads, causal")
+    inp = gen.make_varlen(12, sq, sk, 6, 3, 64, 64, causal=causal)
+    _prefill_check(inp, f"varlen 11 seqs, 3 kv heads, {'causal' if causal else 'no mask'}")
 
 
 def test_prefill_varlen_empty_rows():
