@@ -1436,7 +1436,7 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_mx_kernel(const KParams p)
 // Waves per SIMD of the per-head decode kernel, and the tiles each keeps in flight in registers
 // (DEPTH x (d + dv) / 4 registers of staging). d + dv <= 256 with one 16-row block per wave: two
 // waves per SIMD with one stage each (about 200 registers); on the long-KV decode workload
-// (131072 keys, 8 q heads per kv head) that measured 6% faster than one wave with two stages.
+// (131072 keys, 8 q heads per kv head) that measured 6-7% faster than one wave with two stages.
 // Otherwise one wave per SIMD with the whole 512-entry register file: two stages (faster than
 // three or four when this kernel carried the paged GQA decode workload; the extra requests in
 // flight only lengthen the memory queues), one where two would spill.
