@@ -2227,25 +2227,31 @@ __device__ __forceinline__ PartialRows partial_rows(const CParams& c, int b, int
   return r;
 }
 
-// Log-sum-exp merge of split partials: one thread per 4 output elements of one row.
+// Log-sum-exp merge of split partials: one thread per 4 output elements of one row. IDX32: the
+// launch has fewer than 2^31 threads, so the row and its (b, i, h) come from 32-bit divisions
+// (a 64-bit division by a run-time value is a long instruction sequence ahead of every load).
+template <bool IDX32>
 __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
-  const int tpr = c.dv / 4;
-  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t rows = (int64_t)c.batch * c.max_sq * c.hq;
-  const int64_t row = gt / tpr;
+  typedef typename std::conditional<IDX32, uint32_t, int64_t>::type idx_t;
+  const idx_t tpr = (idx_t)(c.dv / 4);
+  const idx_t gt = (idx_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const idx_t rows = (idx_t)c.batch * c.max_sq * c.hq;
+  const idx_t row = gt / tpr;
   const int q = (int)(gt - row * tpr);
   if (row >= rows) return;
-  const int h = (int)(row % c.hq);
-  const int i = (int)((row / c.hq) % c.max_sq);
-  const int b = (int)(row / ((int64_t)c.hq * c.max_sq));
+  const idx_t rq = row / (idx_t)c.hq;
+  const int h = (int)(row - rq * (idx_t)c.hq);
+  const int b = (int)(rq / (idx_t)c.max_sq);
+  const int i = (int)(rq - (idx_t)b * (idx_t)c.max_sq);
+  // the sequence's query rows and its partial slots are independent loads, issued together
+  const PartialRows pr = partial_rows(c, b, i, h, row, rows);
   const int q0 = c.cu_q ? c.cu_q[b] : 0;
   const int sq = c.cu_q ? c.cu_q[b + 1] - q0 : c.max_sq;
   if (i >= sq) return;
-  const PartialRows pr = partial_rows(c, b, i, h, row, rows);
-  // One pass over the splits in batches of 8 whose LSE and partial loads are all issued before
+  // One pass over the splits in batches of 16 whose LSE and partial loads are all issued before
   // any is used (the kernel is bound by memory latency, not bandwidth): a running max, with the
-  // sums rescaled when a batch raises it, so a problem of up to 8 splits costs one round trip.
-  constexpr int SB = 8;
+  // sums rescaled when a batch raises it, so a problem of up to 16 splits costs one round trip.
+  constexpr int SB = 16;
   // a sink logit is one more denominator term without a value
   const float z = c.sink ? c.sink[h] : kNegInf;
   float mx = z;
@@ -2556,7 +2562,10 @@ hipError_t launch_combine(const CParams& cp, hipStream_t stream) {
   }
   const int64_t threads = rows * (cp.dv / 4);
   const int64_t blocks = (threads + 255) / 256;
-  hipLaunchKernelGGL(fa8_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, cp);
+  if (blocks * 256 < ((int64_t)1 << 31))
+    hipLaunchKernelGGL(fa8_combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, cp);
+  else
+    hipLaunchKernelGGL(fa8_combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, cp);
   return hipGetLastError();
 }
 
