@@ -8,8 +8,8 @@ is the step's K+V bandwidth in GB/s. The causal-prefill workload (B = 2, 8192 x 
 heads, d = 128) is timed next to it and reported in TFLOP/s under "prefill".
 
 Prints one JSON line. Inputs are resident in HBM before timing; the dominant kernel's own
-duration is measured with HIP events on its launch stream around the decode kernel of every step
-of an eager loop.
+average duration is measured with HIP events on its launch stream around a run of back-to-back
+decode launches (and, per launch, around the decode kernel of every step of an eager loop).
 """
 from __future__ import annotations
 
@@ -160,7 +160,9 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
                 attention span of replayed CUDA graphs); the replays' output must equal the eager
                 step's bit for bit;
       eager_ms: the same calls issued eagerly, wall time / steps;
-      kernel_ms: HIP events on the launch stream around the decode kernel of every step of the
+      kernel_ms: HIP events on the launch stream around `steps` decode launches issued back to
+                back, elapsed time / steps;
+      kernel_ms_events (median, quartiles): HIP events around the decode kernel of every step of the
                 eager loop (mean; median and quartiles beside it).
     Returns a dict."""
     q, k, v, kw = device_args(inp, dev)
@@ -217,6 +219,16 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     kt = np.array([a.elapsed_time(b) for a, b in evs])
+    # the decode kernel's average launch duration: `steps` launches issued back to back between
+    # one pair of events on the launch stream (an event pair around each launch also holds that
+    # launch's dispatch latency, a few microseconds)
+    ba, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ba.record()
+    for _ in range(steps):
+        decode()
+    bb.record()
+    torch.cuda.synchronize()
+    batched_ms = ba.elapsed_time(bb) / steps
     ref = out.clone()
     assert torch.isfinite(ref.float()).all(), "non-finite decode output"
     graph = torch.cuda.CUDAGraph()
@@ -238,7 +250,7 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3 / (replays * STEPS_PER_GRAPH)
     assert torch.equal(out, ref), "graph replay differs from the eager decode step"
-    res = dict(count, graph_ms=graph_ms, eager_ms=eager_ms, kernel_ms=float(kt.mean()),
+    res = dict(count, graph_ms=graph_ms, eager_ms=eager_ms, kernel_ms=batched_ms, kernel_ms_events=float(kt.mean()),
                kernel_ms_median=float(np.median(kt)), kernel_ms_q1=float(np.percentile(kt, 25)),
                kernel_ms_q3=float(np.percentile(kt, 75)))
     del graph
@@ -269,20 +281,31 @@ def decode_figures(inp, r: dict) -> dict:
                          f"replayed back to back",
              eager_step_value=gbs(sb, r["eager_ms"]), eager_step_ms=round(r["eager_ms"], 5),
              kernel_value=gbs(kb, r["kernel_ms"]), kernel_ms=round(r["kernel_ms"], 5),
-             kernel_ms_median=round(r["kernel_ms_median"], 5),
-             kernel_ms_quartiles=[round(r["kernel_ms_q1"], 5), round(r["kernel_ms_q3"], 5)],
+             kernel_timing=KERNEL_TIMING,
+             kernel_ms_per_launch_events={"mean": round(r["kernel_ms_events"], 5),
+                                          "median": round(r["kernel_ms_median"], 5),
+                                          "quartiles": [round(r["kernel_ms_q1"], 5), round(r["kernel_ms_q3"], 5)]},
              kernel_pct_of_hbm_peak=round(100 * kb / (r["kernel_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2))
     return d
 
 
 FLUSH_MIB = 512   # more than the L2s and the 256 MB MALL together
+KERNEL_TIMING = ("HIP events on the launch stream around the timed launches issued back to back: "
+                 "elapsed time / launches (per-launch event pairs, which also hold each launch's "
+                 "dispatch latency, are reported beside it)")
 
 
 def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
-    """Wall time per launch and mean HIP-event time of `steps` back-to-back prefill launches after
-    `warmup` untimed ones (inputs resident in HBM, caches warm from the previous launches). With
-    `flushed`, also the mean event time of `steps` launches each preceded by a FLUSH_MIB write that
-    evicts the caches (the write is outside the events), returned third (else None)."""
+    """Prefill launches after `warmup` untimed ones (inputs resident in HBM, caches warm from the
+    previous launches). Returns (wall_ms, kernel_ms, event_ms, flushed_ms):
+      wall_ms, kernel_ms: `steps` launches issued back to back; wall time per launch (synchronize
+          before and after) and the average launch duration from one pair of HIP events around the
+          run on the launch stream;
+      event_ms: the mean of an event pair around each of `steps` more launches (each also holds
+          its launch's dispatch latency);
+      flushed_ms (with `flushed`, else None): the same per-launch event mean over `steps` launches
+          each preceded by a FLUSH_MIB write that evicts the caches (the write is outside the
+          events), to compare with event_ms."""
     q, k, v, kw = device_args(inp, dev)
     if getattr(inp, "sink", None) is not None:
         kw["sink"] = to_dev(np.asarray(inp.sink, np.float32), dev)
@@ -290,17 +313,24 @@ def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
     out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=odt, device=dev)
     for _ in range(warmup):
         binding.prefill(q, k, v, out=out, **kw)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ra.record()
+    for _ in range(steps):
+        binding.prefill(q, k, v, out=out, **kw)
+    rb.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernel_ms = ra.elapsed_time(rb) / steps
+    assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
         a.record()
         binding.prefill(q, k, v, out=out, **kw)
         b.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    event_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     flushed_ms = None
     if flushed:
         buf = torch.empty(FLUSH_MIB << 20, dtype=torch.uint8, device=dev)
@@ -313,26 +343,27 @@ def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
         torch.cuda.synchronize()
         flushed_ms = float(np.mean([a.elapsed_time(b) for a, b in fevs]))
         del buf
-    return (t1 - t0) * 1e3 / steps, kernel_ms, flushed_ms
+    return (t1 - t0) * 1e3 / steps, kernel_ms, event_ms, flushed_ms
 
 
 def bench_prefill_mx(inp, steps: int, warmup: int, dev):
-    """Per-launch kernel time (HIP events) of the MXFP8 prefill on an MX-encoded input."""
+    """Average launch duration of the MXFP8 prefill on an MX-encoded input: one pair of HIP events
+    around `steps` back-to-back launches."""
     q, k, v = (to_dev(x, dev) for x in (inp.q, inp.k, inp.v))
     qs, ks, vs = (to_dev(x, dev) for x in (inp.q_mx, inp.k_mx, inp.v_mx))
     out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=torch.bfloat16, device=dev)
     kw = dict(causal=inp.causal, window_left=inp.window_left, window_right=inp.window_right, out=out)
     for _ in range(warmup):
         binding.prefill_mx(q, k, v, qs, ks, vs, **kw)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    for a, b in evs:
-        a.record()
+    a.record()
+    for _ in range(steps):
         binding.prefill_mx(q, k, v, qs, ks, vs, **kw)
-        b.record()
+    b.record()
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all(), "non-finite MX prefill output"
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return a.elapsed_time(b) / steps
 
 
 def other_workloads(args, dev) -> dict:
@@ -353,7 +384,7 @@ def other_workloads(args, dev) -> dict:
         out[f"long_kv_decode_{path}"] = dict(workload=lk.name, unit="GB/s", **decode_figures(lk, r))
     # the causal prefill workload with a learnable sink logit per query head (N(0, 1))
     cs = gen.with_sink(gen.causal_prefill(2), 12)
-    ms, kms, _ = bench_prefill(cs, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
+    ms, kms, _, _ = bench_prefill(cs, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
     fl = prefill_flop(cs)
     out["causal_prefill_with_sink"] = {"workload": cs.name, "unit": "TFLOP/s",
                                        "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
@@ -393,14 +424,17 @@ def other_workloads(args, dev) -> dict:
         # the same warm-up as the causal prefill: the first ~20 launches on a new set of buffers
         # run up to 15% slower (measured; a cache-evicting write before each launch does not bring
         # that back, so it is not the caches' contents)
-        ms, kms, fms = bench_prefill(mv, args.prefill_steps, args.prefill_warmup, dev, flushed=True)
+        ms, kms, ems, fms = bench_prefill(mv, args.prefill_steps, args.prefill_warmup, dev, flushed=True)
         fl = prefill_flop(mv)
         out[f"mixed_varlen_d{d}x{dv}"] = {"workload": mv.name, "unit": "TFLOP/s",
                                           "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
                                           "kernel_pct_of_fp8_peak": round(100 * fl / (kms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2),
+                                          "kernel_timing": KERNEL_TIMING,
+                                          "per_launch_event_ms": round(ems, 5),
                                           "flushed_kernel_value": round(fl / (fms * 1e-3) / 1e12, 2),
                                           "flushed_kernel_ms": round(fms, 5),
-                                          "flushed_note": f"each launch after a {FLUSH_MIB} MiB write (caches cold)",
+                                          "flushed_note": f"each launch after a {FLUSH_MIB} MiB write (caches cold), an event "
+                                                          f"pair around each launch: compare with per_launch_event_ms",
                                           "flop": fl}
     return out
 
@@ -539,12 +573,12 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(f"fa8_decode_heads_kernel_balanced_{dec.name}_traffic.md"),
-                     "kernel_ms": fig["kernel_ms"], "kernel_ms_median": fig["kernel_ms_median"],
-                     "kernel_ms_quartiles": fig["kernel_ms_quartiles"], "bytes_per_launch": kbytes},
+                     "kernel_ms": fig["kernel_ms"], "kernel_timing": KERNEL_TIMING,
+                     "kernel_ms_per_launch_events": fig["kernel_ms_per_launch_events"], "bytes_per_launch": kbytes},
     }
     if not args.no_prefill:
         pre = gen.causal_prefill(2)
-        p_ms, p_kern, p_flushed = bench_prefill(pre, args.prefill_steps, args.prefill_warmup, dev, flushed=True)
+        p_ms, p_kern, p_events, p_flushed = bench_prefill(pre, args.prefill_steps, args.prefill_warmup, dev, flushed=True)
         flop = prefill_flop(pre)
         tfl = flop / (p_ms * 1e-3) / 1e12
         ktfl = flop / (p_kern * 1e-3) / 1e12
@@ -555,10 +589,12 @@ def main():
                          "achieved": round(ktfl, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(ktfl / FP8_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic(f"fa8_prefill_kernel_{pre.name}_traffic.md"),
-                         "kernel_ms": round(p_kern, 4)},
+                         "kernel_ms": round(p_kern, 4), "kernel_timing": KERNEL_TIMING,
+                         "kernel_ms_per_launch_events": round(p_events, 4)},
             "flushed_kernel_ms": round(p_flushed, 4),
             "flushed_kernel_value": round(flop / (p_flushed * 1e-3) / 1e12, 2),
-            "flushed_note": f"each launch after a {FLUSH_MIB} MiB write (caches cold)",
+            "flushed_note": f"each launch after a {FLUSH_MIB} MiB write (caches cold), an event pair around each "
+                            f"launch: compare with kernel_ms_per_launch_events",
         }
     if not args.no_extra:
         line["other_workloads"] = other_workloads(args, dev)
