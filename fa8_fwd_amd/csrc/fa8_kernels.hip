@@ -518,14 +518,29 @@ __device__ __forceinline__ void qk_tile(const FA8_LDS uint8_t* kt, const v8i (&q
 
 // The rest of a tile given its S^T: mask, row max, lazy rescale of l and O, P, PV onto O and
 // the row sum (the second part of attn_tile).
+// Per-lane part of the LDS offset of the V^T operand for output column block n (the key order
+// of the S^T accumulator, read by ds_read_b64_tr_b8 from the row-major swizzled V tile): the
+// swizzle key of a row depends only on its bits 0, 1 and 3, which the 16-row and 64-row steps
+// of the read leave alone, so row block r of k-step pk adds the constant (64 pk + 16 r) * DV.
+template <int DV>
+__device__ __forceinline__ uint32_t v_lane_offset(int n, int lane) {
+  constexpr int VCH = DV / 16;
+  const int hgrp = lane >> 5;
+  const int trj = (lane & 15) >> 1;
+  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
+  const int tr_chunk_hi = (lane >> 4) & 1;
+  const int tr_byte = 8 * (lane & 1);
+  return (uint32_t)(tr_key * DV + swz<VCH>(2 * n + tr_chunk_hi, v_sv(tr_key)) * 16 + tr_byte);
+}
+
 template <int D, int DV, int BN>
-__device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, v16f (&sacc)[BN / 32], float c,
-                                                bool need_mask, int j0, int my_lo, int my_hi, int lane,
-                                                float& m_run, float& l_run, v16f (&oacc)[DV / 32]) {
+__device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, const uint32_t (&voff)[DV / 32],
+                                                v16f (&sacc)[BN / 32], float c, bool need_mask, int j0, int my_lo,
+                                                int my_hi, int lane, float& m_run, float& nb, float& l_run,
+                                                v16f (&oacc)[DV / 32]) {
   constexpr int KB = BN / 32;        // 32-key blocks of S^T
   constexpr int PK = BN / 64;        // 64-key k-steps of PV
   constexpr int NB = DV / 32;
-  constexpr int VCH = DV / 16;
   const int hgrp = lane >> 5;
 
   // ---- mask (only tiles that cross some row's key bounds): key j is visible iff
@@ -552,19 +567,22 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, v16f 
   float mx = max3f(mxc[0], mxc[1], __builtin_elementwise_maximum(mxc[2], mxc[3]));
   mx = max_xor32(mx);
   const float mt = mx * c;
-  float alpha = 1.0f;
-  if (mt - m_run > kTau) {          // also true when m_run = -inf and mt is finite
-    alpha = fast_exp2(m_run - mt);  // 0 when m_run = -inf
-    m_run = mt;
-  }
-  const float nb = (m_run == kNegInf) ? 0.0f : kBias - m_run;
-
-  // ---- O = alpha * O, only when some row of the wave moved its max (rare once the maxima
-  //      settle): the PV products below accumulate onto O on the matrix cores, whose accumulator
-  //      input is added at fp32 precision on gfx950 (measured: chained accumulation over 128k
-  //      keys matches a separate fp32 fold of per-tile products to within 4e-6 of sum |p v|,
-  //      with no drift), so no separate O_tile and fold are needed ----
-  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+  // ---- rescale, only when some row of the wave moved its max (rare once the maxima settle): the
+  //      new max, alpha = 2^(m_old - m_new) (0 when m_old = -inf), the exponent offset
+  //      nb = 8 - m (kept across tiles) and O = alpha * O. The PV products below accumulate onto
+  //      O on the matrix cores, whose accumulator input is added at fp32 precision on gfx950
+  //      (measured: chained accumulation over 128k keys matches a separate fp32 fold of per-tile
+  //      products to within 4e-6 of sum |p v|, with no drift), so no separate O_tile and fold are
+  //      needed ----
+  const bool up = mt - m_run > kTau;   // also true when m_run = -inf and mt is finite
+  if (__builtin_amdgcn_ballot_w64(up)) {
+    float alpha = 1.0f;
+    if (up) {
+      alpha = fast_exp2(m_run - mt);
+      m_run = mt;
+      nb = kBias - m_run;
+    }
+    l_run *= alpha;
 #pragma unroll
     for (int n = 0; n < NB; n++)
 #pragma unroll
@@ -582,18 +600,11 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, v16f 
   constexpr bool kRowSum16 = DV <= 128;
   const int sel = kRowSum16 ? (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1) ? 0x38383838 : 0) : 0x38383838;
   const v8i rsel = {sel, sel, sel, sel, sel, sel, sel, sel};
-  const int trj = (lane & 15) >> 1;
-  const int tr_key = 8 * (trj >> 2) + 4 * hgrp + (trj & 3);
-  const int tr_chunk_hi = (lane >> 4) & 1;
-  const int tr_byte = 8 * (lane & 1);
   auto v_operand = [&](int pk, int n) {
     v8i vop;
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      const int row = 64 * pk + 16 * r + tr_key;
-      const int ch = 2 * n + tr_chunk_hi;
-      const int off = row * DV + swz<VCH>(ch, v_sv(row)) * 16 + tr_byte;
-      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + off));
+      const v2i x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA8_LDS v2i*)(vt + voff[n] + (64 * pk + 16 * r) * DV));
       vop[2 * r] = x[0];
       vop[2 * r + 1] = x[1];
     }
@@ -623,8 +634,8 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, v16f 
     else
       rs32 = (pk == 0) ? mfma_32x32x64_fp8(rsel, pop, (v16f){}) : mfma_32x32x64_fp8(rsel, pop, rs32);
   }
-  if constexpr (kRowSum16) l_run = alpha * l_run + rs[0];
-  else l_run = alpha * l_run + rs32[0];
+  if constexpr (kRowSum16) l_run += rs[0];
+  else l_run += rs32[0];
 }
 
 // One KV tile of BN keys (LDS K tile at kt, V tile at vt, both row-major and swizzled) for the
@@ -632,11 +643,11 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, v16f 
 template <int D, int DV, int BN>
 __device__ __forceinline__ void attn_tile(const FA8_LDS uint8_t* kt, const FA8_LDS uint8_t* vt,
                                           const v8i (&qop)[(D + 63) / 64], float c, bool need_mask, int j0,
-                                          int my_lo, int my_hi, int lane, float& m_run, float& l_run,
-                                          v16f (&oacc)[DV / 32]) {
+                                          int my_lo, int my_hi, int lane, const uint32_t (&voff)[DV / 32],
+                                          float& m_run, float& nb, float& l_run, v16f (&oacc)[DV / 32]) {
   v16f sacc[BN / 32];
   qk_tile<D, BN>(kt, qop, lane, sacc);
-  softmax_pv_tile<D, DV, BN>(vt, sacc, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+  softmax_pv_tile<D, DV, BN>(vt, voff, sacc, c, need_mask, j0, my_lo, my_hi, lane, m_run, nb, l_run, oacc);
 }
 
 // One 64-key tile for decode, on the 16x16x128 FP8 MFMA: NQB blocks of 16 query rows (decode
@@ -1000,6 +1011,11 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     const int row = pos / DV, pc = (pos - row * DV) >> 4;
     v_off[i] = (uint32_t)(row * (int)ka.v_rs + swz<VCH>(pc, v_sv(row)) * 16);
   }
+  // LDS destination of this wave's first copy instruction into stage 0 (K, then V), uniform
+  const uint32_t kdst0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((FA8_LDS uint8_t*)smem + wave * KINST * 1024));
+  const uint32_t vdst0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((FA8_LDS uint8_t*)smem + KTILE + wave * VINST * 1024));
   auto dma_tile = [&](int t, int st) {
     FA8_LDS uint8_t* kt = (FA8_LDS uint8_t*)smem + st * STAGE;
     FA8_LDS uint8_t* vt = kt + KTILE;
@@ -1010,11 +1026,9 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
       const v4i kr = buffer_rsrc(p.k + ka.kbase + (int64_t)j0 * ka.k_rs, (uint32_t)((rows - 1) * (int)ka.k_rs + D));
       const v4i vr = buffer_rsrc(p.v + ka.vbase + (int64_t)j0 * ka.v_rs, (uint32_t)((rows - 1) * (int)ka.v_rs + DV));
 #pragma unroll
-      for (int i = 0; i < KINST; i++)
-        buffer_copy16_to_lds(kr, k_off[i], (uint32_t)reinterpret_cast<uintptr_t>(kt + (wave * KINST + i) * 1024));
+      for (int i = 0; i < KINST; i++) buffer_copy16_to_lds(kr, k_off[i], kdst0 + st * STAGE + i * 1024);
 #pragma unroll
-      for (int i = 0; i < VINST; i++)
-        buffer_copy16_to_lds(vr, v_off[i], (uint32_t)reinterpret_cast<uintptr_t>(vt + (wave * VINST + i) * 1024));
+      for (int i = 0; i < VINST; i++) buffer_copy16_to_lds(vr, v_off[i], vdst0 + st * STAGE + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < KINST; i++) {
@@ -1037,7 +1051,15 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     }
   };
 
-  float m_run = kNegInf, l_run = 0.0f;
+  // per-lane V operand offsets, computed once and held in registers for the whole loop (the
+  // empty asm keeps the compiler from recomputing them in every tile)
+  uint32_t voff[NB];
+#pragma unroll
+  for (int n = 0; n < NB; n++) {
+    voff[n] = v_lane_offset<DV>(n, lane);
+    __asm__ __volatile__("" : "+v"(voff[n]));
+  }
+  float m_run = kNegInf, nb = 0.0f, l_run = 0.0f;   // nb = 8 - m_run (0 while m_run = -inf)
   v16f oacc[NB];
 #pragma unroll
   for (int n = 0; n < NB; n++)
@@ -1049,16 +1071,30 @@ __global__ void __launch_bounds__(256, 2) fa8_prefill_kernel(const KParams p) {
     wait_vmcnt<0>();
     __syncthreads();
   }
-  for (int t = t_begin; t < t_end; t++) {
-    const int st = (t - t_begin) & 1;
+  // Tile t uses stage (t - t_begin) & 1. For d + dv <= 256 the loop runs two tiles per iteration
+  // so that each tile's stage is a constant: the LDS operand addresses are then one per-lane
+  // register plus an immediate offset, with no per-tile address arithmetic (larger head dims keep
+  // one tile per iteration: the second copy of the loop body would not fit their registers).
+  auto tile = [&](int t, auto stage) __attribute__((always_inline)) {
+    const int st = stage;
     if (t + 1 < t_end) dma_tile(t + 1, st ^ 1);
     const FA8_LDS uint8_t* kt = (const FA8_LDS uint8_t*)smem + st * STAGE;
     const int j0 = t * BN;
     const bool need_mask = (j0 < full_lo) || (j0 + BN > full_hi);
     if (j0 < wv_hi && j0 + BN > wv_lo)
-      attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, m_run, l_run, oacc);
+      attn_tile<D, DV, BN>(kt, kt + KTILE, qop, c, need_mask, j0, my_lo, my_hi, lane, voff, m_run, nb, l_run, oacc);
     wait_vmcnt<0>();   // this wave's loads of tile t+1 have landed in LDS
     __syncthreads();   // ... and every other wave's; all reads of stage st are done
+  };
+  if constexpr (D + DV <= 256) {
+    int t = t_begin;
+    for (; t + 1 < t_end; t += 2) {
+      tile(t, std::integral_constant<int, 0>{});
+      tile(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < t_end) tile(t, std::integral_constant<int, 0>{});
+  } else {
+    for (int t = t_begin; t < t_end; t++) tile(t, (t - t_begin) & 1);
   }
 
   const float l_tot = l_run;   // the MFMA row sums already cover both lanes of a row
