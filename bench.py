@@ -384,7 +384,7 @@ def other_workloads(args, dev) -> dict:
         out[f"long_kv_decode_{path}"] = dict(workload=lk.name, unit="GB/s", **decode_figures(lk, r))
     # the causal prefill workload with a learnable sink logit per query head (N(0, 1))
     cs = gen.with_sink(gen.causal_prefill(2), 12)
-    ms, kms, _, _ = bench_prefill(cs, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
+    ms, kms, _, _ = bench_prefill(cs, max(5, args.prefill_steps // 2), args.prefill_warmup, dev)
     fl = prefill_flop(cs)
     out["causal_prefill_with_sink"] = {"workload": cs.name, "unit": "TFLOP/s",
                                        "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
@@ -413,7 +413,7 @@ def other_workloads(args, dev) -> dict:
     # the MXFP8 variant on the causal prefill shape: N(0,1) data encoded as MXFP8 (E4M3 elements,
     # E8M0 scales per 32 elements of d for Q/K and per 32 keys for V)
     mx = gen.make_mx(2, 2, 8192, 8192, 32, 8, 128, 128, causal=True, name="mxfp8_causal_prefill_b2_s8192_h32x8_d128")
-    kms = bench_prefill_mx(mx, max(5, args.prefill_steps // 2), max(10, args.prefill_warmup // 2), dev)
+    kms = bench_prefill_mx(mx, max(5, args.prefill_steps // 2), args.prefill_warmup, dev)
     fl = prefill_flop(mx)
     out["mxfp8_causal_prefill"] = {"workload": mx.name, "unit": "TFLOP/s",
                                    "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
@@ -421,10 +421,12 @@ def other_workloads(args, dev) -> dict:
     del mx
     for d, dv in ((256, 256), (192, 128)):
         mv = gen.mixed_varlen(4, d=d, dv=dv)
-        # the same warm-up as the causal prefill: the first ~20 launches on a new set of buffers
-        # run up to 15% slower (measured; a cache-evicting write before each launch does not bring
-        # that back, so it is not the caches' contents)
-        ms, kms, ems, fms = bench_prefill(mv, args.prefill_steps, args.prefill_warmup, dev, flushed=True)
+        # twice the causal prefill's warm-up: on a new set of buffers these short launches keep
+        # getting faster for the first 100-200 launches (measured in blocks of 20: d = 256 264,
+        # 247, 240, 233, 229 us, then about 228; (192, 128) 174 ... 139 us after 200; the causal
+        # prefill settles after about 60). A cache-evicting write before each launch does not
+        # bring that back, so it is not the caches' contents
+        ms, kms, ems, fms = bench_prefill(mv, args.prefill_steps, 2 * args.prefill_warmup, dev, flushed=True)
         fl = prefill_flop(mv)
         out[f"mixed_varlen_d{d}x{dv}"] = {"workload": mv.name, "unit": "TFLOP/s",
                                           "kernel_value": round(fl / (kms * 1e-3) / 1e12, 2), "kernel_ms": round(kms, 5),
@@ -519,7 +521,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--prefill-warmup", type=int, default=50)
+    ap.add_argument("--prefill-warmup", type=int, default=100,
+                    help="untimed launches before each prefill leg (the mixed varlen legs take twice as many)")
     ap.add_argument("--num-splits", type=int, default=0,
                     help="static splits of the paged GQA decode figure beside the headline (0 = the library's heuristic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
