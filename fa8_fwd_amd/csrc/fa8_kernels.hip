@@ -576,6 +576,9 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, const
   //      needed ----
   const bool up = mt - m_run > kTau;   // also true when m_run = -inf and mt is finite
   if (__builtin_amdgcn_ballot_w64(up)) {
+    // O is still all zeros while every row of the wave had m = -inf (its first visible tile):
+    // scaling it would change nothing
+    const bool o_live = __builtin_amdgcn_ballot_w64(m_run != kNegInf) != 0;
     float alpha = 1.0f;
     if (up) {
       alpha = fast_exp2(m_run - mt);
@@ -583,10 +586,12 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, const
       nb = kBias - m_run;
     }
     l_run *= alpha;
+    if (o_live) {
 #pragma unroll
-    for (int n = 0; n < NB; n++)
+      for (int n = 0; n < NB; n++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) oacc[n][r] *= alpha;
+        for (int r = 0; r < 16; r++) oacc[n][r] *= alpha;
+    }
   }
 
   // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order, its row sum on the matrix cores and
