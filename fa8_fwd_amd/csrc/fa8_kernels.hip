@@ -2338,21 +2338,26 @@ __global__ void __launch_bounds__(256) fa8_combine_kernel(const CParams c) {
   }
 }
 
-// Combine for many splits: one workgroup per output row, SP split lanes x CGP column groups
-// (CGP = dv / 4 rounded up to a power of two). Split lane sp takes splits sp, sp + SP, ...; the
-// lanes' maxima, weight sums and weighted partial rows meet in LDS. With S = 256 and dv = 128
-// each thread loads 8 splits, all issued together, instead of one row's thread walking 256.
+// Combine for many splits: one workgroup per (output row, block of CGP column groups of 4
+// columns), SP = kWideThreads / CGP split lanes x CGP column groups. Split lane sp takes splits
+// sp, sp + SP, ...; the lanes' maxima, weight sums and weighted partial rows meet in LDS. With
+// S = 256 and dv = 128 each thread loads 8 splits, all issued together, instead of one row's
+// thread walking 256, and each row is spread over four workgroups (a single workgroup reading a
+// row's 256 partials ran at one compute unit's share of the memory bandwidth).
+constexpr int kWideThreads = 256;
 template <int CGP>
-__global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c) {
-  constexpr int SP = 1024 / CGP;
+__global__ void __launch_bounds__(kWideThreads) fa8_combine_wide_kernel(const CParams c) {
+  constexpr int SP = kWideThreads / CGP;
   constexpr int SB = 8;
   __shared__ float s_mx[SP], s_den[SP];
   __shared__ v4f s_acc[SP][CGP];
   const int tid = threadIdx.x;
-  const int q = tid % CGP, sp = tid / CGP;
   const int tpr = c.dv / 4;
+  const int ncb = (tpr + CGP - 1) / CGP;                 // column blocks per row
   const int64_t rows = (int64_t)c.batch * c.max_sq * c.hq;
-  const int64_t row = blockIdx.x;
+  const int64_t row = blockIdx.x / ncb;
+  const int cb = (int)(blockIdx.x - row * ncb);
+  const int q = cb * CGP + tid % CGP, sp = tid / CGP;
   const int h = (int)(row % c.hq);
   const int i = (int)((row / c.hq) % c.max_sq);
   const int b = (int)(row / ((int64_t)c.hq * c.max_sq));
@@ -2394,8 +2399,8 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
       acc += w * o[k];
     }
   }
-  s_acc[sp][q] = acc;
-  if (q == 0) {
+  s_acc[sp][tid % CGP] = acc;
+  if (tid % CGP == 0) {
     s_mx[sp] = mx;
     s_den[sp] = den;
   }
@@ -2413,7 +2418,7 @@ __global__ void __launch_bounds__(1024) fa8_combine_wide_kernel(const CParams c)
     for (int k = 0; k < SP; k++) {
       const float r = (s_mx[k] == kNegInf) ? 0.0f : __expf(s_mx[k] - mx);   // lane with no split: 0
       den += r * s_den[k];
-      acc += r * s_acc[k][q];
+      acc += r * s_acc[k][tid];
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -2594,11 +2599,10 @@ hipError_t launch_combine(const CParams& cp, hipStream_t stream) {
   // workers per sequence (cp.nsplit holds the worker count then)
   const bool wide = cp.sched ? cp.nsplit > 16 * (int64_t)cp.batch : cp.nsplit > 16;
   if (wide && rows < (1 << 20)) {
-    const dim3 grid((unsigned)rows);
-    const int cg = cp.dv / 4;
-    if (cg <= 16) hipLaunchKernelGGL(fa8_combine_wide_kernel<16>, grid, dim3(1024), 0, stream, cp);
-    else if (cg <= 32) hipLaunchKernelGGL(fa8_combine_wide_kernel<32>, grid, dim3(1024), 0, stream, cp);
-    else hipLaunchKernelGGL(fa8_combine_wide_kernel<64>, grid, dim3(1024), 0, stream, cp);
+    constexpr int CGP = 8;
+    const int ncb = (cp.dv / 4 + CGP - 1) / CGP;
+    const dim3 grid((unsigned)(rows * ncb));
+    hipLaunchKernelGGL(fa8_combine_wide_kernel<CGP>, grid, dim3(kWideThreads), 0, stream, cp);
     return hipGetLastError();
   }
   const int64_t threads = rows * (cp.dv / 4);
