@@ -596,14 +596,12 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, const
 
   // ---- P = 2^(S*c - m + 8) as E4M3 in PV-operand order, its row sum on the matrix cores and
   //      O += V^T P^T. Each 64-key half's PV MFMAs follow its own exponentials, so they overlap
-  //      those of the next half. Row sum, dv <= 128: P as the B operand of the 16x16x128 MFMA,
-  //      whose column j collects lanes j, j+16, j+32 and j+48 (both key halves of query rows j
-  //      and j+16); a selector A operand (E4M3 1.0 = 0x38 in lane i+16q when q%2 == (i/4)%2,
-  //      else 0) makes output rows 4(L/16) .. +3 of lane L the sum over the keys of query row
-  //      L%32, the lane's own row, at half the MFMA work of a 32x32 product. dv > 128: an
-  //      all-ones A operand on the 32x32x64 MFMA (no registers to spare for the selector) ----
-  constexpr bool kRowSum16 = DV <= 128;
-  const int sel = kRowSum16 ? (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1) ? 0x38383838 : 0) : 0x38383838;
+  //      those of the next half. Row sum: P as the B operand of the 16x16x128 MFMA, whose column
+  //      j collects lanes j, j+16, j+32 and j+48 (both key halves of query rows j and j+16); a
+  //      selector A operand (E4M3 1.0 = 0x38 in lane i+16q when q%2 == (i/4)%2, else 0) makes
+  //      output rows 4(L/16) .. +3 of lane L the sum over the keys of query row L%32, the lane's
+  //      own row, at half the MFMA work of a 32x32 product ----
+  const int sel = (((lane >> 4) & 1) == (((lane & 15) >> 2) & 1)) ? 0x38383838 : 0;
   const v8i rsel = {sel, sel, sel, sel, sel, sel, sel, sel};
   auto v_operand = [&](int pk, int n) {
     v8i vop;
@@ -616,7 +614,6 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, const
     return vop;
   };
   v4f rs;
-  v16f rs32;
 #pragma unroll
   for (int pk = 0; pk < PK; pk++) {
     v8i pop;
@@ -634,13 +631,9 @@ __device__ __forceinline__ void softmax_pv_tile(const FA8_LDS uint8_t* vt, const
 #pragma unroll
     for (int n = 0; n < NB; n++) oacc[n] = mfma_32x32x64_fp8(v_operand(pk, n), pop, oacc[n]);
     // the row sum after the PV MFMAs of the half: its result is read last
-    if constexpr (kRowSum16)
-      rs = (pk == 0) ? mfma_16x16x128_fp8(rsel, pop, (v4f){0.0f, 0.0f, 0.0f, 0.0f}) : mfma_16x16x128_fp8(rsel, pop, rs);
-    else
-      rs32 = (pk == 0) ? mfma_32x32x64_fp8(rsel, pop, (v16f){}) : mfma_32x32x64_fp8(rsel, pop, rs32);
+    rs = (pk == 0) ? mfma_16x16x128_fp8(rsel, pop, (v4f){0.0f, 0.0f, 0.0f, 0.0f}) : mfma_16x16x128_fp8(rsel, pop, rs);
   }
-  if constexpr (kRowSum16) l_run += rs[0];
-  else l_run += rs32[0];
+  l_run += rs[0];
 }
 
 // One KV tile of BN keys (LDS K tile at kt, V tile at vt, both row-major and swizzled) for the
