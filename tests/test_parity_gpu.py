@@ -284,7 +284,7 @@ def test_long_kv_no_shrinkage():
         assert 0.99 <= ratio <= 1.01
 
 
-@pytest.mark.parametrize("S,DV", [(6, 128), (40, 128), (40, 96), (33, 256), (64, 64)])
+@pytest.mark.parametrize("S,DV", [(6, 128), (40, 128), (40, 96), (40, 192), (33, 256), (64, 64)])
 def test_combine_entry_point_alone(S, DV):
     # random partials with some empty splits, combined on the GPU vs the oracle's combine (more
     # than 16 splits take the split-parallel combine)
