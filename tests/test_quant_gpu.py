@@ -47,6 +47,25 @@ def test_quantizer_bit_exact_varlen_with_zero_and_empty_blocks():
     assert s.cpu().numpy()[1].tolist() == [1.0, 1.0] and s.cpu().numpy()[2, 1] == 1.0
 
 
+def test_quantizer_block_maximum_in_every_chunk_position():
+    # 293 rows = ten 32-row chunks, the last one partial: the max pass takes chunks four at a time
+    # (groups 0-3, 4-7 and the partial 8-9), so each batch puts its block's one large element in
+    # a different chunk (first and last of a group, the partial group, the ragged last rows);
+    # the other kv head's block keeps its maximum in the first row
+    rows, positions = 293, [0, 127, 128, 200, 255, 256, 292]
+    q = _q((len(positions), rows, 4, 64), 9, torch.bfloat16, 0.01)
+    for b, r in enumerate(positions):
+        q[b, r, b % 2, 7] = 3.0 + b          # kv head 0: q heads 0 and 1
+        q[b, 0, 2, 0] = -2.0                 # kv head 1
+    dev = torch.device("cuda:0")
+    got, s = binding.quantize_q(q.to(dev), 2)
+    torch.cuda.synchronize()
+    ref, rs = quant.quantize_q(q.float().numpy(), 2)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.allclose(rs[:, 0], (3.0 + np.arange(len(positions))) / 448.0, rtol=1e-2)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
 def test_quantizer_bit_exact_across_the_scale_range():
     # bf16 blocks whose maxima put s = amax / 448 exactly at 2^-96 (the smallest s of the
     # kernel's short quotient path), one bf16 step below it, among the subnormals, and up to the
