@@ -441,6 +441,90 @@ def other_workloads(args, dev) -> dict:
     return out
 
 
+# The decode steps timed on the Hopper FP8 page ("Native FP8 (E4M3 Q/K/V) forward for Hopper",
+# Performance, decode table: H200 with locked clocks, vLLM's decode launches replayed as CUDA
+# graphs, paged K/V, max_seqlen_k = 32768, the per-layer attention span including the split-KV
+# combine, in microseconds). One rank's heads at the stated tensor parallelism, d = 128, every
+# request "N k" = N * 1024 keys long. Another machine's figures: context, not a target.
+PAGES_DECODE = [
+    # (shape, requests, query tokens per request, keys per request, q heads, kv heads,
+    #  FA3 FP8 us, FA4 native FP8 us on H200)
+    ("Llama-3.1-8B TP1, 1 x 1, 4k", 1, 1, 4096, 32, 8, 17.0, 11.4),
+    ("Llama-3.1-8B TP1, 32 x 1, 2k", 32, 1, 2048, 32, 8, 62.6, 36.2),
+    ("Llama-3.1-8B TP1, 128 x 1, 1k", 128, 1, 1024, 32, 8, 123.1, 74.8),
+    ("Llama-3.1-8B TP1, 16 x 1, 16k", 16, 1, 16384, 32, 8, 189.4, 143.4),
+    ("Llama-3.1-8B TP1, 32 x 4, 4k", 32, 4, 4096, 32, 8, 106.1, 66.1),
+    ("Llama-3.1-70B TP4, 64 x 1, 4k", 64, 1, 4096, 16, 2, 58.5, 40.4),
+    ("Llama-3.1-70B TP4, 8 x 1, 32k", 8, 1, 32768, 16, 2, 57.9, 39.4),
+    ("Qwen3-32B TP2, 32 x 1, 8k", 32, 1, 8192, 32, 4, 102.8, 70.6),
+]
+# K/V pools cycled through by consecutive steps, at least this many MiB in all, so that every
+# step reads its K and V from HBM (the page flushes the L2 between layers; here the L2s and the
+# 256 MB memory-side cache would otherwise hold the smaller shapes' K/V from one step to the next)
+PAGES_ROTATE_MIB = 1024
+
+
+def pages_decode_shapes(dev, replays: int = 8) -> list:
+    """The decode shapes of PAGES_DECODE on this GPU: one decode step = the balanced decode and
+    its combine (16-token pages, a random page permutation, descales in [0.5, 2], causal among a
+    request's query tokens), captured in a HIP graph of at least 16 steps whose consecutive steps
+    read distinct copies of the K/V pools, replayed back to back; wall time per step."""
+    rows = []
+    for idx, (shape, nreq, nq, keys, hq, hkv, fa3_us, fa4_us) in enumerate(PAGES_DECODE):
+        inp = gen.make_paged(40 + idx, [keys] * nreq, hq, hkv, 128, 128, 16, sq=nq, varlen_q=True, causal=nq > 1,
+                             descales=(("uniform", 0.5, 2.0),) * 3, max_seqlen_k=32768, name=shape)
+        q, k, v, kw = device_args(inp, dev)
+        pool = k.numel() + v.numel()
+        copies = int(min(64, max(2, -(-PAGES_ROTATE_MIB * 2 ** 20 // pool))))
+        ks = [k] + [k.clone() for _ in range(copies - 1)]
+        vs = [v] + [v.clone() for _ in range(copies - 1)]
+        B, HQ, SQ, DV = inp.batch, inp.heads_q, inp.max_seqlen_q, inp.dv
+        W = binding.decode_num_workers(q, k, v, **kw)
+        sched = torch.empty(int(binding.load().fa8_decode_schedule_bytes(B)) // 4, dtype=torch.int32, device=dev)
+        op = torch.empty((W + B, SQ, HQ, DV), dtype=torch.float32, device=dev)
+        lp = torch.empty((W + B, SQ, HQ), dtype=torch.float32, device=dev)
+        out = torch.empty((q.shape[0], HQ, DV), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            binding.decode_scheduled(q, ks[i], vs[i], num_workers=W, schedule=sched, o_partial=op, lse_partial=lp,
+                                     **kw)
+            binding.combine_scheduled(op, lp, sched, num_workers=W, batch=B, max_seqlen_q=SQ, heads_q=HQ, dv=DV,
+                                      out=out, cu_seqlens_q=kw["cu_seqlens_q"])
+        for i in range(copies):
+            step(i)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        assert torch.isfinite(ref.float()).all(), f"{shape}: non-finite decode output"
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        nsteps = max(copies, 16)    # at least 16 steps per replay, cycling through the copies
+        with torch.cuda.graph(graph):
+            for i in range(nsteps):
+                step(i % copies)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            graph.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (replays * nsteps)
+        # every copy holds the same values, so every step's output is the eager one's
+        assert torch.equal(out, ref), f"{shape}: graph replay differs from the eager decode step"
+        nbytes = decode_step_bytes(inp)
+        rows.append({"shape": shape, "step_us": round(us, 2), "num_workers": W,
+                     "step_GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "step_bytes": nbytes, "kv_copies": copies,
+                     "page_fa4_native_fp8_h200_us": fa4_us, "page_fa3_fp8_h200_us": fa3_us,
+                     "page_fa4_us_over_this_us": round(fa4_us / us, 3)})
+        del graph, ks, vs, q, k, v, op, lp, out, sched
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -528,6 +612,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long-KV decode and mixed varlen figures")
+    ap.add_argument("--no-pages", action="store_true",
+                    help="skip the decode shapes of the Hopper FP8 page's table (context figures)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time per workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a copy kernel of MIB MiB (for scaling counter passes)")
@@ -601,6 +687,12 @@ def main():
         }
     if not args.no_extra:
         line["other_workloads"] = other_workloads(args, dev)
+    if not args.no_pages:
+        line["pages_decode_shapes"] = {
+            "note": "the decode steps of the Hopper FP8 page's decode table on this GPU (balanced decode + combine, "
+                    "graph-replayed, K/V read from HBM every step), the page's H200 times beside them as context "
+                    "from another machine",
+            "shapes": pages_decode_shapes(dev)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
         if "prefill" in line:
