@@ -153,6 +153,9 @@ typedef struct {
  * needs no separate per-tile fold). FA8_ERR_INVALID also when the launch would need 2^32 or
  * more threads: ceil(max_seqlen_q / 128) x query heads x batch workgroups of 256 threads (for
  * varlen or seqused_k inputs the batch x kv-head count is rounded up to a multiple of 8 first).
+ * The grid is sized from host-side values only, so with varlen inputs every sequence gets the row
+ * blocks of max_seqlen_q; those past a sequence's own length return at once, and a batch of one
+ * long and many short sequences launches mostly such idle workgroups (each costs a dispatch).
  */
 fa8_status fa8_fwd_prefill(const fa8_fwd_params* p, void* stream);
 
