@@ -458,6 +458,12 @@ PAGES_DECODE = [
     ("Llama-3.1-70B TP4, 8 x 1, 32k", 8, 1, 32768, 16, 2, 57.9, 39.4),
     ("Qwen3-32B TP2, 32 x 1, 8k", 32, 1, 8192, 32, 4, 102.8, 70.6),
 ]
+# The table's two Gemma-4-31B rows (TP4, d = 256, 1024-key window; the page gives no head counts,
+# so they are not run): (shape, FA3 FP8 us, FA4 native FP8 us on H200)
+PAGES_DECODE_NOT_RUN = [
+    ("Gemma-4-31B TP4, 4 x 4, 28k", 23.6, 11.4),
+    ("Gemma-4-31B TP4, 16 x 4, 28k", 44.1, 17.0),
+]
 # K/V pools cycled through by consecutive steps, at least this many MiB in all, so that every
 # step reads its K and V from HBM (the page flushes the L2 between layers; here the L2s and the
 # 256 MB memory-side cache would otherwise hold the smaller shapes' K/V from one step to the next)
