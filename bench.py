@@ -144,6 +144,9 @@ def device_args(inp, dev):
     return to_dev(inp.q, dev), to_dev(inp.k, dev), to_dev(inp.v, dev), kw
 
 
+# Runs of back-to-back launches timed for each kernel figure; the median run is reported.
+TIMING_WINDOWS = 3
+
 # Decode steps captured in one HIP graph: a model's forward replays its attention layers inside one
 # graph, back to back; the launch gap of a graph replay comes once per forward, not per layer.
 STEPS_PER_GRAPH = 8
@@ -161,7 +164,7 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
                 step's bit for bit;
       eager_ms: the same calls issued eagerly, wall time / steps;
       kernel_ms: HIP events on the launch stream around `steps` decode launches issued back to
-                back, elapsed time / steps;
+                back, elapsed time / steps (the median of TIMING_WINDOWS such runs);
       kernel_ms_events (median, quartiles): HIP events around the decode kernel of every step of the
                 eager loop (mean; median and quartiles beside it).
     Returns a dict."""
@@ -222,13 +225,17 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
     # the decode kernel's average launch duration: `steps` launches issued back to back between
     # one pair of events on the launch stream (an event pair around each launch also holds that
     # launch's dispatch latency, a few microseconds)
-    ba, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ba.record()
-    for _ in range(steps):
-        decode()
-    bb.record()
-    torch.cuda.synchronize()
-    batched_ms = ba.elapsed_time(bb) / steps
+    # (TIMING_WINDOWS such runs, the median one reported)
+    runs = []
+    for _ in range(TIMING_WINDOWS):
+        ba, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ba.record()
+        for _ in range(steps):
+            decode()
+        bb.record()
+        torch.cuda.synchronize()
+        runs.append(ba.elapsed_time(bb) / steps)
+    batched_ms = float(np.median(runs))
     ref = out.clone()
     assert torch.isfinite(ref.float()).all(), "non-finite decode output"
     graph = torch.cuda.CUDAGraph()
@@ -291,8 +298,8 @@ def decode_figures(inp, r: dict) -> dict:
 
 FLUSH_MIB = 512   # more than the L2s and the 256 MB MALL together
 KERNEL_TIMING = ("HIP events on the launch stream around the timed launches issued back to back: "
-                 "elapsed time / launches (per-launch event pairs, which also hold each launch's "
-                 "dispatch latency, are reported beside it)")
+                 "elapsed time / launches, the median of 3 such runs (per-launch event pairs, which "
+                 "also hold each launch's dispatch latency, are reported beside it)")
 
 
 def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
@@ -300,7 +307,7 @@ def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
     previous launches). Returns (wall_ms, kernel_ms, event_ms, flushed_ms):
       wall_ms, kernel_ms: `steps` launches issued back to back; wall time per launch (synchronize
           before and after) and the average launch duration from one pair of HIP events around the
-          run on the launch stream;
+          run on the launch stream, for the run with the median kernel time of TIMING_WINDOWS;
       event_ms: the mean of an event pair around each of `steps` more launches (each also holds
           its launch's dispatch latency);
       flushed_ms (with `flushed`, else None): the same per-launch event mean over `steps` launches
@@ -313,16 +320,21 @@ def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
     out = torch.empty(tuple(q.shape[:-1]) + (inp.dv,), dtype=odt, device=dev)
     for _ in range(warmup):
         binding.prefill(q, k, v, out=out, **kw)
-    ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ra.record()
-    for _ in range(steps):
-        binding.prefill(q, k, v, out=out, **kw)
-    rb.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernel_ms = ra.elapsed_time(rb) / steps
+    # TIMING_WINDOWS runs of `steps` back-to-back launches; the run with the median kernel time
+    # is reported (one run alone can catch a transient slowdown of the whole GPU)
+    wins = []
+    for _ in range(TIMING_WINDOWS):
+        ra, rb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ra.record()
+        for _ in range(steps):
+            binding.prefill(q, k, v, out=out, **kw)
+        rb.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wins.append((ra.elapsed_time(rb) / steps, (t1 - t0) * 1e3 / steps))
+    kernel_ms, wall_ms = sorted(wins)[len(wins) // 2]
     assert torch.isfinite(out.float()).all(), "non-finite prefill output"
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in evs:
@@ -343,7 +355,7 @@ def bench_prefill(inp, steps: int, warmup: int, dev, flushed: bool = False):
         torch.cuda.synchronize()
         flushed_ms = float(np.mean([a.elapsed_time(b) for a, b in fevs]))
         del buf
-    return (t1 - t0) * 1e3 / steps, kernel_ms, event_ms, flushed_ms
+    return wall_ms, kernel_ms, event_ms, flushed_ms
 
 
 def bench_prefill_mx(inp, steps: int, warmup: int, dev):
