@@ -159,9 +159,9 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
       "static":   fa8_fwd_decode_splitkv with the library's split count + fa8_combine.
     Three timings, with the inputs resident in HBM:
       graph_ms: STEPS_PER_GRAPH steps captured once in a HIP graph and replayed until `steps`
-                steps have run, wall time / steps (the pages time decode as the per-layer
-                attention span of replayed CUDA graphs); the replays' output must equal the eager
-                step's bit for bit;
+                steps have run, wall time / steps, the median of TIMING_WINDOWS such runs (the
+                pages time decode as the per-layer attention span of replayed CUDA graphs); the
+                replays' output must equal the eager step's bit for bit;
       eager_ms: the same calls issued eagerly, wall time / steps;
       kernel_ms: HIP events on the launch stream around `steps` decode launches issued back to
                 back, elapsed time / steps (the median of TIMING_WINDOWS such runs);
@@ -250,12 +250,15 @@ def bench_decode_step(inp, steps: int, warmup: int, dev, path: str = "balanced",
     replays = max(1, -(-steps // STEPS_PER_GRAPH))
     for _ in range(max(1, warmup // STEPS_PER_GRAPH)):
         graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(replays):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - t0) * 1e3 / (replays * STEPS_PER_GRAPH)
+    gruns = []
+    for _ in range(TIMING_WINDOWS):      # the median of TIMING_WINDOWS runs of `replays` replays
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            graph.replay()
+        torch.cuda.synchronize()
+        gruns.append((time.perf_counter() - t0) * 1e3 / (replays * STEPS_PER_GRAPH))
+    graph_ms = float(np.median(gruns))
     assert torch.equal(out, ref), "graph replay differs from the eager decode step"
     res = dict(count, graph_ms=graph_ms, eager_ms=eager_ms, kernel_ms=batched_ms, kernel_ms_events=float(kt.mean()),
                kernel_ms_median=float(np.median(kt)), kernel_ms_q1=float(np.percentile(kt, 25)),
